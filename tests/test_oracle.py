@@ -1,0 +1,336 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Runs on the CPU only. Each test names the fact it pins; together they are
+chosen so that a plausible slip in the oracle (a dropped term, a wrong sign or
+index, a transposed operand, a wrong scale or position) fails at least one.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+from oracle import mla_oracle as om
+from kv_cache_compression_mla_amd import inputs as gen
+from _common import make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def weights64(inp):
+    dt = inp.cfg.dtype
+    return {k: (None if v is None else gen.to_f64(v, dt)) for k, v in inp.weights.items()}
+
+
+def small_v3(B=2, ctx=(5, 70), **kw):
+    return gen.CONFIGS["v3_b1_ctx4k"].with_(name="small_v3", B=B, ctx=tuple(ctx), **kw)
+
+
+# --------------------------------------------------------------------------
+# Storage rounding
+# --------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch_on_float32_values():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000),
+        # exact ties between neighbouring bfloat16 values (round to even)
+        (1.0 + (2 * np.arange(1, 200) + 1) * 2.0 ** -8) * 2.0 ** rng.integers(-30, 30, 199),
+        -(1.0 + (2 * np.arange(1, 200) + 1) * 2.0 ** -8),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(om.bf16_round(x.astype(np.float64)), ref)
+
+
+def test_bf16_round_closed_forms():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties go to the even neighbour 1.
+    assert om.bf16_round(1.0 + 2.0 ** -8) == 1.0
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: even is 1 + 2^-6.
+    assert om.bf16_round(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert om.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    assert om.bf16_round(-3.0) == -3.0 and om.bf16_round(0.0) == 0.0
+    # generator and oracle agree on what bfloat16 means
+    x = np.random.default_rng(2).standard_normal(5000).astype(np.float32)
+    np.testing.assert_array_equal(gen.bf16_bits_to_f64(gen.f32_to_bf16_bits(x)),
+                                  om.bf16_round(x.astype(np.float64)))
+
+
+# --------------------------------------------------------------------------
+# Rotary embedding ("Understanding MLA", section 4)
+# --------------------------------------------------------------------------
+
+def test_rope_identity_at_position_zero_and_norm_preserving():
+    x = np.random.default_rng(3).standard_normal((7, 64))
+    np.testing.assert_array_equal(om.rope(x, 0, 10000.0), x)
+    for pos in (1, 17, 8192, 32768):
+        y = om.rope(x, pos, 10000.0)
+        np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1),
+                                   rtol=1e-13)
+        # each consecutive pair keeps its own length: pairs are rotated, not mixed
+        np.testing.assert_allclose(np.hypot(y[:, 0::2], y[:, 1::2]),
+                                   np.hypot(x[:, 0::2], x[:, 1::2]), rtol=1e-12)
+
+
+def test_rope_two_dimensional_case_is_plain_rotation():
+    # d = 2: a single pair with frequency theta^0 = 1, i.e. the textbook 2x2
+    # rotation by pos radians (counter-clockwise).
+    for pos in (0, 1, 5, 100):
+        np.testing.assert_allclose(om.rope(np.array([1.0, 0.0]), pos, 10000.0),
+                                   [math.cos(pos), math.sin(pos)], atol=1e-15)
+        np.testing.assert_allclose(om.rope(np.array([0.0, 1.0]), pos, 10000.0),
+                                   [-math.sin(pos), math.cos(pos)], atol=1e-15)
+
+
+def test_rope_relative_position_property():
+    # (R_m q) . (R_n k) depends on n - m only.
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for m, n, shift in ((3, 10, 1000), (0, 5000, 77), (8000, 2, 123)):
+        a = om.rope(q, m, 10000.0) @ om.rope(k, n, 10000.0)
+        b = om.rope(q, m + shift, 10000.0) @ om.rope(k, n + shift, 10000.0)
+        c = q @ om.rope(k, n - m, 10000.0)
+        assert abs(a - b) <= 1e-10 * max(1.0, abs(a))
+        assert abs(a - c) <= 1e-10 * max(1.0, abs(a))
+    # and the frequencies really differ per pair: equal rotation of every pair
+    # would leave pair-pair dot products unchanged, which RoPE does not.
+    e = np.zeros(64); e[0] = 1.0
+    f = np.zeros(64); f[62] = 1.0
+    assert not np.allclose(om.rope(e, 7, 1e4)[:2], om.rope(f, 7, 1e4)[62:])
+
+
+# --------------------------------------------------------------------------
+# RMSNorm of the latent ("Understanding MLA", Phase A, A2)
+# --------------------------------------------------------------------------
+
+def test_rms_norm_closed_forms():
+    c = np.full(512, 3.0)
+    np.testing.assert_allclose(om.rms_norm(c, np.ones(512), eps=0.0), np.ones(512), rtol=1e-15)
+    np.testing.assert_allclose(om.rms_norm(c, np.ones(512), eps=1e-6),
+                               np.ones(512) * 3.0 / math.sqrt(9.0 + 1e-6), rtol=1e-15)
+    x = np.random.default_rng(5).standard_normal(512)
+    g = np.random.default_rng(6).standard_normal(512)
+    y = om.rms_norm(x, g, eps=0.0)
+    np.testing.assert_allclose(om.rms_norm(7.5 * x, g, eps=0.0), y, rtol=1e-13)
+    np.testing.assert_allclose(np.sqrt(np.mean((y / g) ** 2)), 1.0, rtol=1e-13)
+    # the norm is nonlinear: W RMSNorm(c) != RMSNorm(W c) in general
+    W = np.random.default_rng(7).standard_normal((512, 512))
+    assert not np.allclose(W @ om.rms_norm(x, np.ones(512)), om.rms_norm(W @ x, np.ones(512)))
+
+
+# --------------------------------------------------------------------------
+# Cache arithmetic printed on the pages
+# --------------------------------------------------------------------------
+
+def _golden():
+    vals = {}
+    with open(os.path.join(GOLDEN, "cache_arithmetic.txt")) as f:
+        for line in f:
+            line = line.split("|")[0].strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = float(v)
+    return vals
+
+
+def test_cache_arithmetic_against_printed_figures():
+    g = _golden()
+    v3 = gen.CONFIGS["v3_b64_ctx8k"]
+    mla = v3.d_c + v3.d_R
+    mha = v3.H * ((v3.d_h + v3.d_R) + v3.d_v)
+    assert mla == g["v3_mla_values_per_token_layer"]
+    assert mha == g["v3_mha_values_per_token_layer"]
+    assert round(mha / mla) == g["v3_mla_vs_mha_ratio_approx"]
+    assert v3.H * (v3.d_h + v3.d_v) == g["v3_per_head_content_values_replaced"]
+    bytes_per_token = mla * 2 * int(g["v3_layers"])
+    assert bytes_per_token == 70272
+    assert round(bytes_per_token / 1000) == g["v3_cache_bytes_per_token_approx_kb"]
+    # DeepSeek-V2 geometry (same latent widths, 60 layers, 128 heads of 128)
+    v2_mla = mla * int(g["v2_layers"])
+    v2_mha = 2 * 128 * 128 * int(g["v2_layers"])
+    assert v2_mla == g["v2_mla_scalars_per_token"]
+    assert v2_mla * 2 / 1024 == g["v2_mla_kib_per_token_fp16"]
+    assert v2_mha == g["v2_mha_scalars_per_token"]
+    assert v2_mha * 2 / 1024 / 1000 == pytest.approx(g["v2_mha_kib_thousands_fp16"], abs=0.005)
+    assert round(v2_mha / v2_mla) == g["v2_mla_vs_mha_ratio_approx"]
+    assert 2 * 128 * 128 / v3.d_c == g["v2_latent_fraction_of_stacked_kv"]
+
+
+# --------------------------------------------------------------------------
+# The attention step
+# --------------------------------------------------------------------------
+
+def _oracle_steps(inp, b, dtype=None, absorbed=False):
+    cfg = inp.cfg
+    W = weights64(inp)
+    h = gen.to_f64(inp.h_t[b], cfg.dtype)
+    prior = gen.to_f64(inp.rows(b, int(inp.ctx[b])), cfg.dtype)
+    f = om.decode_step_absorbed if absorbed else om.decode_step
+    return f(h, prior, W, int(inp.ctx[b]), cfg.theta, cfg.scale, dtype or cfg.dtype,
+             None if W["gamma_kv"] is None else W["gamma_kv"])
+
+
+@pytest.mark.parametrize("cfg", [
+    gen.CONFIGS["tiny_fp32"],
+    gen.CONFIGS["tiny_fp32"].with_(w_std=0.5, seed=11),        # peaked softmax
+    small_v3(B=2, ctx=(1, 300)),
+    small_v3(B=1, ctx=(100,), gamma=True, seed=3),
+    gen.CONFIGS["v3_b128_ragged_paged"].with_(B=2, ctx_range=(60, 200), seed=5),
+])
+def test_absorbed_equals_unabsorbed(cfg):
+    """Q_nope . (W_K c) = (Q_nope W_K) . c ("Understanding MLA", section 4) and
+    the value projection commutes with the weighted sum: both forms agree to
+    1e-10 relative in float64."""
+    inp = make_inputs(cfg)
+    for b in range(cfg.B):
+        u = _oracle_steps(inp, b)
+        a = _oracle_steps(inp, b, absorbed=True)
+        np.testing.assert_array_equal(u["row"], a["row"])
+        for k in ("o", "out"):
+            err = np.abs(u[k] - a[k]).max()
+            assert err <= 1e-10 * np.abs(u[k]).max(), (k, err)
+
+
+def test_single_token_context_returns_that_value_exactly():
+    """With one row the softmax weight is exactly 1, so o(i) = W_UV(i) c_0 and
+    the latent output is c_0 itself."""
+    for cfg in (gen.CONFIGS["tiny_fp32"].with_(ctx=(0,)), small_v3(B=1, ctx=(0,))):
+        inp = make_inputs(cfg)
+        W = weights64(inp)
+        u = _oracle_steps(inp, 0)
+        a = _oracle_steps(inp, 0, absorbed=True)
+        c0 = u["row"][:cfg.d_c]
+        np.testing.assert_array_equal(a["o_lat"], np.broadcast_to(c0, a["o_lat"].shape))
+        ref = np.einsum("ivc,c->iv", W["W_UV"], c0)
+        np.testing.assert_allclose(u["o"], ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("cfg", [gen.CONFIGS["tiny_fp32"],
+                                 gen.CONFIGS["tiny_fp32"].with_(w_std=0.5, seed=11),
+                                 gen.CONFIGS["tiny_fp32"].with_(ctx=(9,), d_cq=24, seed=2)])
+def test_brute_force_matches_oracle(cfg):
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    h = gen.to_f64(inp.h_t[0], cfg.dtype)
+    prior = gen.to_f64(inp.rows(0, int(inp.ctx[0])), cfg.dtype)
+    pos = int(inp.ctx[0])
+    Wl = {k: (None if v is None else v.tolist()) for k, v in W.items()}
+    row, o, out = brute.brute_step(h.tolist(), prior.tolist(), Wl, pos, cfg.theta, cfg.scale,
+                                   lambda v: float(np.float32(v)))
+    ref = om.decode_step(h, prior, W, pos, cfg.theta, cfg.scale, "fp32")
+    np.testing.assert_allclose(row, ref["row"], rtol=0, atol=0)
+    np.testing.assert_allclose(np.array(o), ref["o"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(np.array(out), ref["out"], rtol=1e-11, atol=1e-14)
+
+
+def test_position_shift_leaves_outputs_unchanged():
+    """Rotary scores depend only on offsets ("Understanding MLA", section 4): if
+    every cached key and the query move by the same number of positions, the
+    step's output does not change. History is built by the method itself."""
+    cfg = gen.CONFIGS["tiny_fp32"].with_(w_std=0.3)
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    rng = np.random.default_rng(9)
+    hs = rng.standard_normal((12, cfg.d))
+    outs = []
+    for shift in (0, 5, 1000):
+        prior = np.stack([om.compress_row(hs[u], W["W_DKV"], W["W_KR"], u + shift, cfg.theta)
+                          for u in range(11)])
+        r = om.decode_step(hs[11], prior, W, 11 + shift, cfg.theta, cfg.scale, "fp64")
+        outs.append(r["out"])
+    for o in outs[1:]:
+        np.testing.assert_allclose(o, outs[0], rtol=1e-11, atol=1e-12 * np.abs(outs[0]).max())
+    # and the position does matter when only the query moves
+    prior = np.stack([om.compress_row(hs[u], W["W_DKV"], W["W_KR"], u, cfg.theta)
+                      for u in range(11)])
+    moved = om.decode_step(hs[11], prior, W, 40, cfg.theta, cfg.scale, "fp64")["out"]
+    assert not np.allclose(moved, outs[0], rtol=1e-6)
+
+
+def test_attention_core_matches_torch_sdpa():
+    """Once K and V are rebuilt, the step is textbook scaled dot-product
+    attention with key width d_h + d_R and value width d_v."""
+    cfg = small_v3(B=1, ctx=(257,))
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    h = gen.to_f64(inp.h_t[0], cfg.dtype)
+    prior = gen.to_f64(inp.rows(0, 257), cfg.dtype)
+    r = om.decode_step(h, prior, W, 257, cfg.theta, cfg.scale, cfg.dtype)
+    rows = np.concatenate([prior, r["row"][None]], 0)
+    c, kR = rows[:, :cfg.d_c], rows[:, cfg.d_c:]
+    H = 8   # a subset of heads keeps this quick
+    K = np.stack([np.concatenate([c @ W["W_UK"][i].T, kR], 1) for i in range(H)])
+    V = np.stack([c @ W["W_UV"][i].T for i in range(H)])
+    q = np.concatenate([r["qC"][:H], r["qR"][:H]], 1)[:, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        scale=cfg.scale)[0, :, 0].numpy()
+    np.testing.assert_allclose(r["o"][:H], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_zero_query_gives_mean_of_values():
+    """q = 0 makes every score 0, so softmax is uniform and o is the mean of V."""
+    rng = np.random.default_rng(10)
+    H, d_h, d_c, d_R, L = 3, 16, 32, 8, 37
+    rows = rng.standard_normal((L, d_c + d_R))
+    W_UK, W_UV = rng.standard_normal((H, d_h, d_c)), rng.standard_normal((H, 16, d_c))
+    o = om.attend_unabsorbed(np.zeros((H, d_h)), np.zeros((H, d_R)), rows, W_UK, W_UV, 0.3)
+    ref = np.einsum("ivc,c->iv", W_UV, rows[:, :d_c].mean(0))
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+    o_lat, lse = om.attend_absorbed(np.zeros((H, d_c)), np.zeros((H, d_R)), rows, 0.3)
+    np.testing.assert_allclose(o_lat, np.broadcast_to(rows[:, :d_c].mean(0), o_lat.shape),
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(L), rtol=1e-14)
+
+
+def test_latent_output_is_convex_combination_of_cached_latents():
+    cfg = small_v3(B=1, ctx=(500,))
+    inp = make_inputs(cfg)
+    a = _oracle_steps(inp, 0, absorbed=True)
+    rows = np.concatenate([gen.to_f64(inp.rows(0, 500), "bf16"), a["row"][None]], 0)
+    lo, hi = rows[:, :cfg.d_c].min(0), rows[:, :cfg.d_c].max(0)
+    assert np.all(a["o_lat"] >= lo - 1e-12) and np.all(a["o_lat"] <= hi + 1e-12)
+    # lse is consistent with the scores it normalises
+    q = a["q"]
+    s = (rows @ q.T) * cfg.scale
+    np.testing.assert_allclose(a["lse"], np.log(np.exp(s - s.max(0)).sum(0)) + s.max(0),
+                               rtol=1e-13)
+
+
+def test_dominant_score_selects_its_row():
+    """A query aligned with one cached latent far more than with the others puts
+    (almost) all weight on that row: o_lat -> that row's latent."""
+    rng = np.random.default_rng(12)
+    L, d_c, d_R = 50, 32, 8
+    rows = rng.standard_normal((L, d_c + d_R))
+    q_lat = 60.0 * rows[17:18, :d_c] / np.linalg.norm(rows[17, :d_c]) ** 2 * 10
+    o_lat, _ = om.attend_absorbed(q_lat, np.zeros((1, d_R)), rows, 1.0)
+    np.testing.assert_allclose(o_lat[0], rows[17, :d_c], atol=1e-9)
+
+
+def test_query_without_low_rank_uses_hidden_state_directly():
+    cfg = gen.CONFIGS["tiny_fp32"]
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    h = gen.to_f64(inp.h_t[0], "fp32")
+    qC, qR = om.query(h, None, W["W_UQ"], W["W_QR"], 0, cfg.theta)
+    np.testing.assert_allclose(qC[2], W["W_UQ"][2] @ h, rtol=1e-14)
+    np.testing.assert_allclose(qR[1], W["W_QR"][1] @ h, rtol=1e-14)   # pos 0: no rotation
+
+
+def test_generator_layout_and_poison():
+    cfg = gen.CONFIGS["v3_b128_ragged_paged"].with_(B=3, ctx_range=(60, 200), seed=1)
+    inp = make_inputs(cfg)
+    assert inp.block_table.shape[0] == 3
+    used = inp.block_table[inp.block_table >= 0]
+    assert len(set(used.tolist())) == used.size == inp.cache.shape[0]
+    for b in range(3):
+        n = int(inp.ctx[b])
+        assert not np.isnan(gen.to_f64(inp.rows(b, n), "bf16")).any()
+        assert np.isnan(gen.to_f64(inp.row(b, n), "bf16")).all()   # append slot
+    c = gen.CONFIGS["v3_b64_ctx8k"]
+    assert gen.context_lengths(c).tolist() == [8192] * 64
+    r = gen.context_lengths(gen.CONFIGS["v3_b128_ragged_paged"])
+    assert r.min() >= 1024 and r.max() <= 16384 and r.size == 128
