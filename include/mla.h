@@ -1,0 +1,202 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA decode library, libmla.so.
+ *
+ * One decode step of Multi-head Latent Attention with weight absorption, as
+ * four calls in the order the step runs:
+ *
+ *   mla_compress_append  new token -> cached row [c_KV ; k_R] at its position
+ *   mla_absorb_q         new token -> absorbed query q = [W_UK^T q_C ; q_R]
+ *   mla_decode_attn      q x latent cache -> latent-space output o_lat (+ lse)
+ *   mla_out_proj         o_lat -> per-head outputs W_UV o_lat -> W_O [..]
+ *
+ * Sources (pages): "Understanding MLA (Multi-head Latent Attention)" by
+ * S. Dong (called [DONG] below), "Multi-Head Latent Attention" in the
+ * llm-arch-kb (called [KB]) and the aicassindra "Multi-head latent attention"
+ * explainer (called [CASS]). Notation follows [KB] section 2: h_t is the new
+ * token's hidden state (width d), c_KV its latent (width d_c), k_R its rotary
+ * key (width d_R), H query heads with nope width d_h and value width d_v,
+ * and an optional query latent of width d_cq (d_c' on the pages).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Weights are row-major in the orientation W in R^{out x in} (so a vector v
+ *    maps to W v), per-head weights as [H][out][in]:
+ *      W_DKV [d_c][d]        W_KR [d_R][d]        W_DQ [d_cq][d]
+ *      W_UQ  [H][d_h][d_cq]  W_QR [H][d_R][d_cq]   (in = d when d_cq == 0)
+ *      W_UK  [H][d_h][d_c]   W_UV [H][d_v][d_c]   W_O [d][H*d_v]
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent);
+ *    the structs mla_dims and mla_cache are HOST memory, read during the call
+ *    only. Storage dtype (dims.dtype) applies to h_t, weights, cache, q,
+ *    o_heads and out; o_lat and lse are always float32.
+ *  - Alignment: every device pointer must be 16-byte aligned.
+ *  - The caller owns all memory. The library never allocates device memory
+ *    for a call, never frees, and keeps no pointer after returning; scratch
+ *    space comes from the caller's workspace (see mla_workspace_bytes).
+ *  - Calls are asynchronous: they validate on the host, enqueue kernels on
+ *    `stream` (a hipStream_t; NULL = the default stream) and return. A
+ *    non-zero status means nothing was enqueued (except MLA_ERR_HIP, which
+ *    reports a launch failure). Device faults surface at the caller's
+ *    synchronisation. Device-side preconditions (positions below capacity,
+ *    block-table entries inside the pool) are the caller's to keep.
+ *  - The calls are re-entrant; calls that share output or workspace buffers
+ *    on different streams race.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,         /* a required pointer is NULL                     */
+  MLA_ERR_SHAPE = 2,        /* non-positive or inconsistent sizes             */
+  MLA_ERR_DTYPE = 3,        /* dtype is not MLA_FP32 or MLA_BF16              */
+  MLA_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned        */
+  MLA_ERR_WORKSPACE = 5,    /* ws_bytes below what the call needs             */
+  MLA_ERR_UNSUPPORTED = 6,  /* shape with no compiled kernel                  */
+  MLA_ERR_HIP = 7           /* the HIP runtime reported an error              */
+} mla_status;
+
+typedef enum { MLA_FP32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Layer geometry and scalars ([KB] section 2; [DONG] section 3). */
+typedef struct {
+  int32_t d;              /* hidden width                                     */
+  int32_t H;              /* query heads                                      */
+  int32_t d_h;            /* per-head nope (content) query/key width          */
+  int32_t d_v;            /* per-head value width                             */
+  int32_t d_c;            /* KV latent width                                  */
+  int32_t d_R;            /* decoupled rotary key width (even)                */
+  int32_t d_cq;           /* query latent width; 0 = no query low-rank        */
+  float softmax_scale;    /* 0 -> 1/sqrt(d_h + d_R) ([DONG] D2)               */
+  float rope_theta;       /* rotary base, > 0 (10000 in the DeepSeek configs)  */
+  float norm_eps;         /* latent RMSNorm epsilon; 0 -> 1e-6                 */
+  int32_t dtype;          /* mla_dtype: storage dtype                          */
+} mla_dims;
+
+/*
+ * The latent cache: one row of d_c + d_R values per cached token, the latent
+ * followed by the already-rotated rotary key ([DONG] section 5: the two
+ * objects side by side; [KB] "Per-token cache after decoupling").
+ *  - contiguous (block_table == NULL): data is [B][capacity][d_c + d_R];
+ *    row u of sequence b is at data + (b*capacity + u) * row_bytes.
+ *  - paged (block_table != NULL): data is a pool [n_blocks][block_size][d_c+d_R];
+ *    block_table is a DEVICE int32 array [B][max_blocks]; row u of sequence b
+ *    is slot u % block_size of block block_table[b*max_blocks + u/block_size].
+ */
+typedef struct {
+  void* data;                 /* device                                        */
+  const int32_t* block_table; /* device, or NULL for the contiguous layout     */
+  int32_t capacity;           /* contiguous: rows per sequence                 */
+  int32_t block_size;         /* paged: rows per block                         */
+  int32_t max_blocks;         /* paged: entries per block-table row            */
+  int32_t n_blocks;           /* paged: blocks in the pool                     */
+} mla_cache;
+
+/*
+ * mla_compress_append -- compress the new tokens and append them.
+ * For each sequence b, with t = pos[b]:
+ *   c   = W_DKV h_t[b]                      ([KB] "Low-rank latent"; [DONG] A1)
+ *   c   = c * gamma / sqrt(mean(c^2) + eps) only if gamma_kv != NULL ([DONG] A2)
+ *   k_R = RoPE(W_KR h_t[b], t)              ([KB] "Decoupled RoPE head"; [DONG] B2)
+ * and stores [c ; k_R], rounded to the storage dtype (nearest-even), as row t
+ * of sequence b. RoPE rotates consecutive pairs (x[2j], x[2j+1]) by the angle
+ * t * theta^(-2j/d_R).
+ *   h_t      [B][d]        storage dtype
+ *   gamma_kv [d_c]         storage dtype, or NULL (no latent norm)
+ *   pos      [B] int32     device: position of the new token (= rows already
+ *                          cached); must be < capacity, or inside the
+ *                          sequence's allocated blocks when paged
+ *   ws       workspace of at least mla_workspace_bytes(...) bytes
+ * Only row pos[b] of each sequence is written.
+ */
+mla_status mla_compress_append(const mla_dims* dims, int32_t B, const void* h_t,
+                               const void* W_DKV, const void* W_KR,
+                               const void* gamma_kv, const int32_t* pos,
+                               const mla_cache* cache, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * mla_absorb_q -- the absorbed query of the new tokens.
+ *   c_Q      = W_DQ h_t[b]          (c_Q = h_t[b] when d_cq == 0, W_DQ NULL)
+ *   q_C(i)   = W_UQ(i) c_Q          ([KB] "Query-side compression")
+ *   q_R(i)   = RoPE(W_QR(i) c_Q, pos[b])  (same position as the key, [DONG] C2)
+ *   q_lat(i) = W_UK(i)^T q_C(i)     (the key up-projection moved onto the
+ *                                    query, [DONG] section 4)
+ * Output q [B][H][d_c + d_R] in the storage dtype: q_lat followed by q_R,
+ * the same width as a cache row so attention is one contraction over it.
+ */
+mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t,
+                        const void* W_DQ, const void* W_UQ, const void* W_QR,
+                        const void* W_UK, const int32_t* pos, void* q,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mla_decode_attn -- every head attends against the shared latent cache.
+ * For sequence b, head i and rows u < seq_lens[b]:
+ *   s(i,u)   = scale * (q(b,i) . row(b,u))      over all d_c + d_R columns
+ *   o_lat(i) = sum_u softmax_u(s(i,u)) * row(b,u)[0:d_c]
+ *   lse(i)   = ln sum_u exp(s(i,u))
+ * ([CASS] "End-to-end flow": content and rotary dot products summed, softmax
+ * over all history, weights applied to the cached latents.)
+ *   q          [B][H][d_c + d_R] storage dtype (from mla_absorb_q)
+ *   seq_lens   [B] int32 device: rows attended, the new token included; 0 gives
+ *              an all-zero o_lat row and lse = -inf
+ *   max_seq_len host upper bound of seq_lens (sizes the launch)
+ *   num_splits context splits per sequence, 0 = automatic; the context is cut
+ *              into equal chunks and merged exactly afterwards
+ *   o_lat      [B][H][d_c] float32 out;  lse [B][H] float32 out, or NULL
+ */
+mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q,
+                           const mla_cache* cache, const int32_t* seq_lens,
+                           int32_t max_seq_len, int32_t num_splits,
+                           float* o_lat, float* lse, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * mla_out_proj -- back to the hidden width.
+ *   o_heads(b,i) = W_UV(i) o_lat(b,i)       ([CASS] value projection after the
+ *                                            weighted sum)
+ *   out(b)       = W_O [o_heads(b,1); ...; o_heads(b,H)]  ([DONG] D2)
+ *   o_lat  [B][H][d_c] float32;  o_heads [B][H][d_v] out (storage dtype);
+ *   W_O / out may both be NULL to stop after the per-head outputs.
+ */
+mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat,
+                        const void* W_UV, const void* W_O, void* o_heads,
+                        void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes that suffice for every call above with these sizes
+ * (num_splits as passed to mla_decode_attn, 0 = automatic). 0 on bad dims. */
+size_t mla_workspace_bytes(const mla_dims* dims, int32_t B, int32_t max_seq_len,
+                           int32_t num_splits);
+
+/* The split count mla_decode_attn will use (resolves 0 = automatic); 0 on
+ * bad dims. Needs the current device's compute-unit count for the automatic
+ * choice. */
+int32_t mla_decode_num_splits(const mla_dims* dims, int32_t B, int32_t max_seq_len,
+                              int32_t num_splits);
+
+/* Bytes of one cache row: (d_c + d_R) * element size; 0 on bad dims. */
+size_t mla_cache_row_bytes(const mla_dims* dims);
+
+/* Which attention kernel mla_decode_attn uses for these dims:
+ * 1 = bf16 MFMA kernel (d_c = 512, d_R = 64, H a multiple of 32 up to 128),
+ * 2 = general kernel (any other geometry, fp32 or bf16), 0 = bad dims. */
+int32_t mla_decode_kernel(const mla_dims* dims);
+
+/* Text for a status code (static storage). */
+const char* mla_status_str(int32_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

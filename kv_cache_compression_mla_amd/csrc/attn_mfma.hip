@@ -1,0 +1,397 @@
+// Latent-space MLA decode attention on gfx950 bf16 MFMA.
+//
+// Every query head attends directly against the shared latent cache: the
+// absorbed query q(i) = [W_UK(i)^T q_C(i) ; q_R(i)] is dotted with whole
+// 576-wide rows [c_u ; kR_u], and the softmax weights combine the latents
+// c_u themselves ("Understanding MLA" (Dong), section 4: the key
+// up-projection moves onto the query; aicassindra MLA explainer, "End-to-end
+// flow": content and rotary dot products summed, softmax over all history).
+//
+// Work decomposition: one workgroup = one sequence x one context chunk x all
+// H heads, one wave per 32 heads. The heads that share a latent row form a
+// dense contraction:
+//   S^T[row][head] = K_tile[row][0:576] . Q^T[0:576][head]     (MFMA 32x32x16)
+//   O^T[col][head] += V_tile^T[col][rows] . P[rows][head]      (MFMA 32x32x16)
+// with V_tile = K_tile[:, 0:512]. A wave keeps its query block (32 heads x
+// 576, bf16) in VGPRs and its O^T accumulator (512 x 32 fp32) in AGPRs for
+// the whole chunk.
+//
+// Memory path: each 32-row tile is copied HBM -> LDS once per workgroup by
+// LDS-DMA (global_load_lds, 16 B per lane), four stages deep, so nothing is
+// staged in registers. In LDS the latent part is row-major (1 KiB per row)
+// with 16-byte chunks XOR-swizzled per row, the rotary part is packed 128 B
+// per row with its own swizzle. The score operand is read with ds_read_b128
+// (lanes walk rows); the value operand, whose reduction index is the row, is
+// read transposed with ds_read_b64_tr_b16 from the same row-major copy. Both
+// patterns are bank-conflict free.
+//
+// Softmax is online in base 2 (scale*log2(e) folded in) against a reference
+// maximum m_ref that only moves when a tile's maximum exceeds it by more than
+// 2^64. Below that gap the exponent's reference point simply stays (weights
+// up to 2^64 are exact in fp32/bf16 range and the final division by l removes
+// the common factor). Above it, everything accumulated so far weighs less than
+// 2^-64 per row (below 2^-49 in total for 2^15 rows) against the new maximum's
+// own row, i.e. under fp32 resolution, so the accumulation restarts from zero
+// at the new reference. The accumulator is therefore never rescaled and is
+// only ever touched by MFMA instructions: accumulate, zero (0*0 + 0) and
+// copy-out (0*0 + O), which keeps it resident in AGPRs.
+//
+// Context splits: a workgroup covers rows [s*chunk, min((s+1)*chunk, L_b)).
+// With more than one split it writes unnormalised (O, m, l) partials, merged
+// exactly by attn_combine.
+#include "mla_internal.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int DC = 512;               // latent width
+constexpr int DW = 576;               // row width (latent + rotary key)
+constexpr int TILE = 32;              // rows per stage
+constexpr int LAT_BYTES = TILE * 1024;
+constexpr int STAGE = LAT_BYTES + TILE * 128;   // 36 KiB
+constexpr int NSTAGE = 4;
+constexpr int NTHREADS = 256;
+constexpr int DMA_PER_WAVE = 9;       // 8 latent rows + 1 rotary block per tile
+// A tile whose maximum exceeds the reference by more than this (log2 units)
+// restarts the accumulation at the new maximum; below it the reference stays,
+// so probabilities stay in (0, 2^64].
+constexpr float RESTART_GAP = 64.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+struct Params {
+  const uint16_t* __restrict__ q;
+  const uint16_t* __restrict__ cache;
+  const int32_t* __restrict__ table;
+  long long seq_stride;   // contiguous: capacity * DW elements
+  int bs_log2, max_blocks;
+  const int32_t* __restrict__ seq_lens;
+  int H, chunk, splits;
+  float sl2;              // softmax scale * log2(e)
+  float* o_lat;
+  float* lse;
+  float* part_o;
+  float* part_ml;
+};
+
+// Swizzle of the 16-byte chunk position inside a latent row (a bijection of
+// the low 4 bits): conflict-free for 16 lanes reading 16 rows of one chunk and
+// for 32 lanes transposed-reading 4 rows x 32 columns.
+__device__ __forceinline__ int lat_sw(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ int rope_sw(int r) { return (r >> 1) & 7; }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+// [15:14], expcnt[6:4], lgkmcnt[11:8]; unconstrained fields at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Row u of sequence b. Called with wave-uniform arguments only; the block
+// table is read through the constant address space so that the read is a
+// scalar load (it must not wait on the vector-memory counter, which also
+// tracks the LDS-DMA copies in flight).
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+template <bool PAGED>
+__device__ __forceinline__ const uint16_t* row_ptr(const Params& p, int b, int u) {
+  if constexpr (!PAGED) {
+    return p.cache + b * p.seq_stride + static_cast<long long>(u) * DW;
+  } else {
+    const const_i32* tab = (const const_i32*)(p.table);
+    const int blk = tab[b * p.max_blocks + (u >> p.bs_log2)];
+    return p.cache + ((static_cast<long long>(blk) << p.bs_log2) + (u & ((1 << p.bs_log2) - 1))) * DW;
+  }
+}
+
+// One LDS-DMA copy: every lane moves 16 bytes from its global address to LDS
+// at lds_base + 16 * lane. Written as inline asm so that the compiler does not
+// add its own (conservative, vmcnt(0)) waits in front of later LDS reads; the
+// kernel waits for these copies explicitly (wait_vmcnt + barrier). The copy
+// has no register result, and its address operands are read at issue.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(gptr) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// Issue this wave's 9 LDS-DMA copies of tile rows [r0, r0+32) into stage
+// buffer at LDS address `st`: latent parts of rows 8w..8w+7 (1 KiB each) and
+// the rotary parts of the same 8 rows (128 B each, one copy). Rows at or past
+// row_end are replaced by row_end-1 (a real row, later masked out of the
+// softmax), so no invalid address is ever read. w, r0, row_end are uniform.
+template <bool PAGED>
+__device__ __forceinline__ void issue_tile(const Params& p, uint32_t st, int b, int r0, int row_end,
+                                           int w, int lane) {
+  const uint16_t* rp[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rp[k] = row_ptr<PAGED>(p, b, min(r0 + 8 * w + k, row_end - 1));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = 8 * w + k;
+    dma16(rp[k] + 8 * (lane ^ lat_sw(r)), st + r * 1024);
+  }
+  // rotary block: lane -> row 8w + (lane >> 3), chunk (lane & 7) ^ rope_sw(row)
+  const int j = lane >> 3;
+  const uint16_t* mine = rp[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) mine = (j == k) ? rp[k] : mine;
+  const int c = (lane & 7) ^ rope_sw(8 * w + j);
+  dma16(mine + DC + 8 * c, st + LAT_BYTES + w * 1024);
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int NW, bool PAGED>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_mfma_kernel(Params p) {
+  __shared__ __align__(1024) char smem[NSTAGE * STAGE];
+  const uint32_t smem_lds = lds_addr(smem);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int s_idx = blockIdx.x % p.splits;
+  const int b = blockIdx.x / p.splits;
+
+  const int L = p.seq_lens[b];
+  const int row_begin = s_idx * p.chunk;
+  const int row_end = min(row_begin + p.chunk, L);
+  const bool active = w < NW;
+  const int head = 32 * w + l32;
+
+  if (row_begin >= row_end) {
+    // Nothing to attend in this chunk. With splits > 1 the combine kernel
+    // skips it; with a single split the sequence is empty.
+    if (p.splits == 1 && active) {
+      float* o = p.o_lat + (static_cast<long long>(b) * p.H + head) * DC;
+      for (int c = h * 256; c < h * 256 + 256; c += 4)
+        *reinterpret_cast<f32x4*>(o + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p.lse && h == 0) p.lse[b * p.H + head] = -INFINITY;
+    }
+    return;
+  }
+  const int ntiles = (row_end - row_begin + TILE - 1) / TILE;
+
+  // Query of this lane's head in MFMA B-operand order: step s, half h holds
+  // columns 16s + 8h .. 16s + 8h + 7.
+  bf16x8 qreg[36];
+  if (active) {
+    const uint16_t* qp = p.q + (static_cast<long long>(b) * p.H + head) * DW + 8 * h;
+#pragma unroll
+    for (int s = 0; s < 36; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+  }
+
+  // Prologue: tiles 0..NSTAGE-2 in flight. Then wait for everything issued so
+  // far (the query and these copies) so that no vector-memory wait remains
+  // pending inside the loop: the loop's waits are the explicit ones below.
+#pragma unroll
+  for (int j = 0; j < NSTAGE - 1; ++j)
+    if (j < ntiles) issue_tile<PAGED>(p, smem_lds + j * STAGE, b, row_begin + j * TILE, row_end, w, lane);
+  wait_vmcnt<0>();
+
+  const bf16x8 zero8 = {};
+  f32x16 oacc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(oacc[i]) : "v"(zero8));
+  float m_ref = -INFINITY;   // reference maximum, log2 units
+  float l_run = 0.f;         // this lane's partial sum (its 16 of each 32 rows)
+
+  // Per-lane LDS byte offsets inside a stage; everything that varies with the
+  // unrolled loop indices below is a compile-time immediate on top of these.
+  // Score operand (lanes = rows): latent chunk c = 2s + h of row l32 sits at
+  // 16 * ((c & ~15) | ((c & 15) ^ lat_sw(l32))).
+  int qk_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qk_off[j] = l32 * 1024 + 16 * ((2 * j + h) ^ lat_sw(l32));
+  int rp_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rp_off[j] = LAT_BYTES + l32 * 128 + 16 * ((2 * j + h) ^ rope_sw(l32));
+  // Value operand, transposed read: in its 16-lane group a lane supplies row
+  // r = 16t + 8k + 4*(g16>>1) + tr_e and columns col = 32cb + 16*(g16&1) + 4*tr_q.
+  // With lat_sw(r) = 4*tr_e + ((2k + (g16>>1)) & 3) the swizzled address is
+  // 16384t + 8192k + 256*(cb>>2) + tr_off[k][cb&3].
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tr_e = i16 >> 2, tr_q = i16 & 3;
+  int tr_off[2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int lowx = (2 * (g16 & 1) + (tr_q >> 1)) ^ ((2 * k + (g16 >> 1)) & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      tr_off[k][j] = (4 * (g16 >> 1) + tr_e) * 1024 + 64 * (j ^ tr_e) + 16 * lowx + 8 * (tr_q & 1);
+  }
+
+  for (int it = 0; it < ntiles; ++it) {
+    // Tile `it` was issued NSTAGE-1 iterations ago; later tiles may still fly.
+    const int later = min(ntiles - 1 - it, NSTAGE - 2);
+    if (later >= 2) wait_vmcnt<2 * DMA_PER_WAVE>();
+    else if (later == 1) wait_vmcnt<DMA_PER_WAVE>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (it + NSTAGE - 1 < ntiles)
+      issue_tile<PAGED>(p, smem_lds + ((it + NSTAGE - 1) % NSTAGE) * STAGE, b,
+                 row_begin + (it + NSTAGE - 1) * TILE, row_end, w, lane);
+    if (!active) continue;
+
+    const char* st = smem + (it % NSTAGE) * STAGE;
+    const int nv = min(TILE, row_end - (row_begin + it * TILE));
+
+    // ---- scores: S^T[row][head] over all 576 columns ----
+    // Operand reads run two steps ahead of the MFMA that consumes them.
+    auto qk_operand = [&](int s) -> bf16x8 {
+      const char* ap = (s < 32) ? st + qk_off[s & 7] + 256 * (s >> 3) : st + rp_off[s - 32];
+      return *reinterpret_cast<const bf16x8*>(ap);
+    };
+    f32x16 sacc;
+    bf16x8 a0 = qk_operand(0), a1 = qk_operand(1);
+#pragma unroll
+    for (int s = 0; s < 36; ++s) {
+      const bf16x8 a2 = (s + 2 < 36) ? qk_operand(s + 2) : a0;
+      if (s == 0) {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(a0), "v"(qreg[s]));
+      } else {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(a0), "v"(qreg[s]));
+      }
+      a0 = a1;
+      a1 = a2;
+    }
+    // The VALU reads the MFMA result next: the wait states are tied to sacc so
+    // that no read of it can be scheduled ahead of them.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc));
+
+    // ---- online softmax (base 2) with a lazily moved reference max ----
+    if (nv < TILE) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * h + (r & 3) >= nv) sacc[r] = -INFINITY;
+    }
+    float tmax = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.sl2;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + RESTART_GAP) != 0) {
+      // Restart at the new maximum (rare: at most a few times per chunk).
+      m_ref = fmaxf(m_ref, tmax);
+      l_run = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(oacc[i]) : "v"(zero8));
+    }
+    float psum = 0.f;
+    float pv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.sl2, -m_ref));
+      psum += pv[r];
+    }
+    l_run += psum;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bf16x2 v2 = __builtin_convertvector((f32x2{pv[8 * t + 2 * k], pv[8 * t + 2 * k + 1]}), bf16x2);
+        pb[t][2 * k] = v2[0];
+        pb[t][2 * k + 1] = v2[1];
+      }
+
+    // P was just written by the VALU and is read by MFMAs next (VALU-write to
+    // MFMA-read wait states, tied to the operands).
+    asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]));
+    // ---- O^T[col][head] += V^T P ----
+    // Transposed operand reads run one (cb, t) step ahead of their MFMA.
+    auto pv_operand = [&](int cb, int t) -> bf16x8 {
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(st + 16384 * t + 256 * (cb >> 2) + tr_off[0][cb & 3]));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(st + 16384 * t + 8192 + 256 * (cb >> 2) + tr_off[1][cb & 3]));
+      return __builtin_bit_cast(bf16x8, (s16x8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+    };
+    bf16x8 v0 = pv_operand(0, 0), v1 = pv_operand(0, 1);
+#pragma unroll
+    for (int step = 0; step < 32; ++step) {
+      const int cb = step >> 1, t = step & 1;
+      const bf16x8 v2 = (step + 2 < 32) ? pv_operand((step + 2) >> 1, (step + 2) & 1) : v0;
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(oacc[cb]) : "v"(v0), "v"(pb[t]));
+      v0 = v1;
+      v1 = v2;
+    }
+  }
+
+  if (!active) return;
+  // The accumulators are read next; cover the last MFMAs' latency.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = (p.splits == 1) ? 1.f / l_tot : 1.f;
+  float* o = (p.splits == 1)
+                 ? p.o_lat + (static_cast<long long>(b) * p.H + head) * DC
+                 : p.part_o + ((static_cast<long long>(b) * p.splits + s_idx) * p.H + head) * DC;
+  o += 4 * h;
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb) {
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[cb][r]));
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<f32x4*>(o + 32 * cb + 8 * g) =
+          f32x4{x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv};
+  }
+  if (h == 0) {
+    if (p.splits == 1) {
+      if (p.lse) p.lse[b * p.H + head] = (m_ref + log2f(l_tot)) * 0.69314718055994531f;
+    } else {
+      const long long pidx = (static_cast<long long>(b) * p.splits + s_idx) * p.H + head;
+      p.part_ml[pidx * 2] = m_ref;
+      p.part_ml[pidx * 2 + 1] = l_tot;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
+  Params p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.cache = static_cast<const uint16_t*>(a.cache);
+  p.table = a.block_table;
+  p.seq_stride = a.capacity * DW;
+  p.bs_log2 = a.block_table ? __builtin_ctz(static_cast<unsigned>(a.block_size)) : 0;
+  p.max_blocks = a.max_blocks;
+  p.seq_lens = a.seq_lens;
+  p.H = a.H;
+  p.chunk = a.chunk;
+  p.splits = a.splits;
+  p.sl2 = a.scale * 1.4426950408889634f;
+  p.o_lat = a.o_lat;
+  p.lse = a.lse;
+  p.part_o = a.part_o;
+  p.part_ml = a.part_ml;
+  const dim3 grid(a.B * a.splits);
+  const bool paged = a.block_table != nullptr;
+#define MLA_ATTN_LAUNCH(NW)                                                          \
+  if (paged) attn_mfma_kernel<NW, true><<<grid, NTHREADS, 0, stream>>>(p);           \
+  else attn_mfma_kernel<NW, false><<<grid, NTHREADS, 0, stream>>>(p);
+  switch (a.H / 32) {
+    case 1: MLA_ATTN_LAUNCH(1) break;
+    case 2: MLA_ATTN_LAUNCH(2) break;
+    case 3: MLA_ATTN_LAUNCH(3) break;
+    case 4: MLA_ATTN_LAUNCH(4) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MLA_ATTN_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,387 @@
+// C ABI of libmla.so: host-side validation, workspace carving and dispatch.
+// See include/mla.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "mla.h"
+#include "mla_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mla_status ok() {
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == MLA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+mla_status check_dims(const mla_dims* d) {
+  if (!d) return fail(MLA_ERR_NULL, "dims is NULL");
+  if (d->dtype != MLA_FP32 && d->dtype != MLA_BF16) return fail(MLA_ERR_DTYPE, "dtype %d", d->dtype);
+  if (d->d <= 0 || d->H <= 0 || d->d_h <= 0 || d->d_v <= 0 || d->d_c <= 0 || d->d_R <= 0 || d->d_cq < 0)
+    return fail(MLA_ERR_SHAPE, "non-positive size in dims");
+  if (d->d_R % 2) return fail(MLA_ERR_SHAPE, "d_R must be even (rotary pairs)");
+  if (d->d_c > 1024 || d->d_c + d->d_R > 2048)
+    return fail(MLA_ERR_UNSUPPORTED, "d_c > 1024 or d_c + d_R > 2048");
+  if (!(d->rope_theta > 0.f)) return fail(MLA_ERR_SHAPE, "rope_theta must be > 0");
+  if (d->softmax_scale < 0.f || std::isnan(d->softmax_scale)) return fail(MLA_ERR_SHAPE, "softmax_scale");
+  // Rows must be 16-byte multiples so every row start stays 16-byte aligned.
+  if (((d->d_c + d->d_R) * elem_size(d->dtype)) % 16)
+    return fail(MLA_ERR_ALIGN, "cache row bytes must be a multiple of 16");
+  return MLA_OK;
+}
+
+float softmax_scale(const mla_dims* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt(static_cast<float>(d->d_h + d->d_R));
+}
+
+mla_status check_cache(const mla_dims* d, const mla_cache* c) {
+  if (!c) return fail(MLA_ERR_NULL, "cache is NULL");
+  if (!c->data) return fail(MLA_ERR_NULL, "cache.data is NULL");
+  if (!aligned16(c->data)) return fail(MLA_ERR_ALIGN, "cache.data not 16-byte aligned");
+  if (c->block_table) {
+    if (c->block_size <= 0 || c->max_blocks <= 0 || c->n_blocks <= 0)
+      return fail(MLA_ERR_SHAPE, "paged cache sizes must be positive");
+    if (c->block_size & (c->block_size - 1)) return fail(MLA_ERR_UNSUPPORTED, "block_size must be a power of two");
+    if (!aligned16(c->block_table)) return fail(MLA_ERR_ALIGN, "block_table not 16-byte aligned");
+  } else if (c->capacity <= 0) {
+    return fail(MLA_ERR_SHAPE, "contiguous cache capacity must be positive");
+  }
+  (void)d;
+  return MLA_OK;
+}
+
+int device_cus() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
+  return v;
+}
+
+bool mfma_attn(const mla_dims* d) {
+  return d->dtype == MLA_BF16 && d->d_c == 512 && d->d_R == 64 && d->H % 32 == 0 && d->H <= 128;
+}
+
+// Split count and rows per split for the attention launch.
+void attn_plan(const mla_dims* d, int B, int max_seq_len, int num_splits, int* splits, int* chunk) {
+  const int L = max_seq_len > 0 ? max_seq_len : 1;
+  int s = num_splits;
+  if (s <= 0) {
+    const int cus = device_cus();
+    s = (cus + B - 1) / B;                  // about one workgroup per compute unit
+    const int min_rows = 256;
+    const int smax = (L + min_rows - 1) / min_rows;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+  }
+  if (s > L) s = L;
+  int ch = (L + s - 1) / s;
+  if (mfma_attn(d)) ch = (ch + 31) / 32 * 32;   // whole 32-row tiles per split
+  *chunk = ch;
+  *splits = (L + ch - 1) / ch;
+}
+
+struct GemmShape { int M, N, K, G; };
+
+int splits_for(const GemmShape& s, int dtype) { return mla::gemm_splits(s.M, s.N, s.K, s.G, dtype); }
+
+size_t part_bytes(const GemmShape& s, int dtype) {
+  return static_cast<size_t>(splits_for(s, dtype)) * s.G * s.M * s.N * sizeof(float);
+}
+
+size_t ws_compress(const mla_dims* d, int B) {
+  return align_up(part_bytes({B, d->d_c, d->d, 1}, d->dtype)) + align_up(part_bytes({B, d->d_R, d->d, 1}, d->dtype));
+}
+
+size_t ws_absorb(const mla_dims* d, int B) {
+  const size_t es = elem_size(d->dtype);
+  const int qin = d->d_cq ? d->d_cq : d->d;
+  size_t p = 0;
+  if (d->d_cq) p = part_bytes({B, d->d_cq, d->d, 1}, d->dtype);
+  p = std::max(p, part_bytes({B, d->H * d->d_h, qin, 1}, d->dtype));
+  p = std::max(p, part_bytes({B, d->H * d->d_R, qin, 1}, d->dtype));
+  p = std::max(p, part_bytes({B, d->d_c, d->d_h, d->H}, d->dtype));
+  return align_up(static_cast<size_t>(B) * d->d_cq * es) + align_up(static_cast<size_t>(B) * d->H * d->d_h * es) +
+         align_up(p);
+}
+
+size_t ws_attn(const mla_dims* d, int B, int max_seq_len, int num_splits) {
+  int s = 1, ch = 1;
+  attn_plan(d, B, max_seq_len, num_splits, &s, &ch);
+  if (s <= 1) return 0;
+  return align_up(static_cast<size_t>(B) * s * d->H * d->d_c * sizeof(float)) +
+         align_up(static_cast<size_t>(B) * s * d->H * 2 * sizeof(float));
+}
+
+size_t ws_out(const mla_dims* d, int B) {
+  return align_up(std::max(part_bytes({B, d->d_v, d->d_c, d->H}, d->dtype),
+                           part_bytes({B, d->d, d->H * d->d_v, 1}, d->dtype)));
+}
+
+mla_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MLA_OK;
+}
+
+#define MLA_TRY(expr)               \
+  do {                              \
+    mla_status _s = (expr);         \
+    if (_s != MLA_OK) return _s;    \
+  } while (0)
+
+mla_status gemm(const void* A, long long lda, long long sAg, bool a_f32, const void* W, long long ldw,
+                long long sWg, bool w_kn, const GemmShape& s, int dtype, float* P, hipStream_t st) {
+  mla::GemmArgs g{A, lda, sAg, a_f32, W, ldw, sWg, w_kn, s.M, s.N, s.K, s.G, splits_for(s, dtype), P, dtype};
+  return hip_status(mla::launch_gemm(g, st), "gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: invalid or inconsistent sizes";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unsupported dtype";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: pointer or row not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for this shape";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+    default: return "unknown mla_status";
+  }
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+size_t mla_cache_row_bytes(const mla_dims* dims) {
+  if (check_dims(dims) != MLA_OK) return 0;
+  return static_cast<size_t>(dims->d_c + dims->d_R) * elem_size(dims->dtype);
+}
+
+int32_t mla_decode_kernel(const mla_dims* dims) {
+  if (check_dims(dims) != MLA_OK) return 0;
+  return mfma_attn(dims) ? 1 : 2;
+}
+
+int32_t mla_decode_num_splits(const mla_dims* dims, int32_t B, int32_t max_seq_len, int32_t num_splits) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  int s = 1, ch = 1;
+  attn_plan(dims, B, max_seq_len, num_splits, &s, &ch);
+  return s;
+}
+
+size_t mla_workspace_bytes(const mla_dims* dims, int32_t B, int32_t max_seq_len, int32_t num_splits) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  size_t w = ws_compress(dims, B);
+  w = std::max(w, ws_absorb(dims, B));
+  w = std::max(w, ws_attn(dims, B, max_seq_len, num_splits));
+  w = std::max(w, ws_out(dims, B));
+  return std::max<size_t>(w, 256);
+}
+
+mla_status mla_compress_append(const mla_dims* dims, int32_t B, const void* h_t, const void* W_DKV,
+                               const void* W_KR, const void* gamma_kv, const int32_t* pos,
+                               const mla_cache* cache, void* ws, size_t ws_bytes, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
+  if (!h_t || !W_DKV || !W_KR || !pos || !ws) return fail(MLA_ERR_NULL, "compress_append: NULL pointer");
+  MLA_TRY(check_cache(dims, cache));
+  for (const void* p : {h_t, W_DKV, W_KR, static_cast<const void*>(pos), static_cast<const void*>(ws)})
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "compress_append: pointer not 16-byte aligned");
+  if (gamma_kv && !aligned16(gamma_kv)) return fail(MLA_ERR_ALIGN, "gamma_kv not 16-byte aligned");
+  const size_t need = ws_compress(dims, B);
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "compress_append needs %zu bytes", need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = dims->dtype;
+  const bool f32 = dt == MLA_FP32;
+  char* w = static_cast<char*>(ws);
+  float* Pc = reinterpret_cast<float*>(w);
+  float* Pr = reinterpret_cast<float*>(w + align_up(part_bytes({B, dims->d_c, dims->d, 1}, dt)));
+  const GemmShape sc{B, dims->d_c, dims->d, 1}, sr{B, dims->d_R, dims->d, 1};
+  MLA_TRY(gemm(h_t, dims->d, 0, f32, W_DKV, dims->d, 0, false, sc, dt, Pc, st));
+  MLA_TRY(gemm(h_t, dims->d, 0, f32, W_KR, dims->d, 0, false, sr, dt, Pr, st));
+  const float eps = dims->norm_eps > 0.f ? dims->norm_eps : 1e-6f;
+  MLA_TRY(hip_status(mla::launch_append(Pc, splits_for(sc, dt), Pr, splits_for(sr, dt), B, dims->d_c, dims->d_R,
+                                        gamma_kv, eps, pos, dims->rope_theta, *cache, dt, st),
+                     "append launch"));
+  return ok();
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const void* W_DQ,
+                        const void* W_UQ, const void* W_QR, const void* W_UK, const int32_t* pos,
+                        void* q, void* ws, size_t ws_bytes, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
+  if (!h_t || !W_UQ || !W_QR || !W_UK || !pos || !q || !ws) return fail(MLA_ERR_NULL, "absorb_q: NULL pointer");
+  if ((dims->d_cq > 0) != (W_DQ != nullptr))
+    return fail(MLA_ERR_NULL, "absorb_q: W_DQ must be given iff d_cq > 0");
+  for (const void* p : {h_t, W_UQ, W_QR, W_UK, static_cast<const void*>(pos), static_cast<const void*>(q),
+                        static_cast<const void*>(ws)})
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "absorb_q: pointer not 16-byte aligned");
+  if (W_DQ && !aligned16(W_DQ)) return fail(MLA_ERR_ALIGN, "absorb_q: W_DQ not 16-byte aligned");
+  const size_t need = ws_absorb(dims, B);
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "absorb_q needs %zu bytes", need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = dims->dtype;
+  const size_t es = elem_size(dt);
+  const bool f32 = dt == MLA_FP32;
+  const int H = dims->H, d_h = dims->d_h, d_R = dims->d_R, d_c = dims->d_c, D = d_c + d_R;
+  char* w = static_cast<char*>(ws);
+  void* cq = w;
+  void* qC = w + align_up(static_cast<size_t>(B) * dims->d_cq * es);
+  float* P = reinterpret_cast<float*>(static_cast<char*>(qC) + align_up(static_cast<size_t>(B) * H * d_h * es));
+  // c_Q = W_DQ h (or h itself)
+  const void* cin = h_t;
+  int qin = dims->d;
+  if (dims->d_cq) {
+    const GemmShape s{B, dims->d_cq, dims->d, 1};
+    MLA_TRY(gemm(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, st));
+    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), 1, B, dims->d_cq, cq, dims->d_cq, 0, dt, st),
+                       "reduce launch"));
+    cin = cq;
+    qin = dims->d_cq;
+  }
+  // q_C(i) = W_UQ(i) c_Q for all heads at once: W_UQ viewed as [H*d_h][qin]
+  {
+    const GemmShape s{B, H * d_h, qin, 1};
+    MLA_TRY(gemm(cin, qin, 0, f32, W_UQ, qin, 0, false, s, dt, P, st));
+    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), 1, B, H * d_h, qC, H * d_h, 0, dt, st),
+                       "reduce launch"));
+  }
+  // q_R(i) = RoPE(W_QR(i) c_Q, pos) into q[b][i][d_c:]
+  {
+    const GemmShape s{B, H * d_R, qin, 1};
+    MLA_TRY(gemm(cin, qin, 0, f32, W_QR, qin, 0, false, s, dt, P, st));
+    void* qr = static_cast<char*>(q) + static_cast<size_t>(d_c) * es;
+    MLA_TRY(hip_status(mla::launch_reduce_rope(P, splits_for(s, dt), B, H, d_R, pos, dims->rope_theta, qr,
+                                               static_cast<long long>(H) * D, D, dt, st),
+                       "rope launch"));
+  }
+  // q_lat(i) = W_UK(i)^T q_C(i): per head g, A_g[b][k] = qC[b][g*d_h + k],
+  // W_g(n=c, k) = W_UK[g][k][c] (k-major use of the [d_h][d_c] matrix).
+  {
+    const GemmShape s{B, d_c, d_h, H};
+    MLA_TRY(gemm(qC, static_cast<long long>(H) * d_h, d_h, f32, W_UK, d_c, static_cast<long long>(d_h) * d_c,
+                 true, s, dt, P, st));
+    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), H, B, d_c, q, static_cast<long long>(H) * D,
+                                                D, dt, st),
+                       "reduce launch"));
+  }
+  return ok();
+}
+
+mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
+                           const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_lat,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
+  if (max_seq_len < 0 || num_splits < 0) return fail(MLA_ERR_SHAPE, "negative max_seq_len or num_splits");
+  if (!q || !seq_lens || !o_lat) return fail(MLA_ERR_NULL, "decode_attn: NULL pointer");
+  MLA_TRY(check_cache(dims, cache));
+  if (!cache->block_table && max_seq_len > cache->capacity)
+    return fail(MLA_ERR_SHAPE, "max_seq_len %d exceeds capacity %d", max_seq_len, cache->capacity);
+  if (cache->block_table &&
+      static_cast<long long>(max_seq_len) > static_cast<long long>(cache->max_blocks) * cache->block_size)
+    return fail(MLA_ERR_SHAPE, "max_seq_len exceeds max_blocks * block_size");
+  for (const void* p : {q, static_cast<const void*>(seq_lens), static_cast<const void*>(o_lat)})
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "decode_attn: pointer not 16-byte aligned");
+  int splits = 1, chunk = 1;
+  attn_plan(dims, B, max_seq_len, num_splits, &splits, &chunk);
+  const size_t need = ws_attn(dims, B, max_seq_len, num_splits);
+  if (need && (!ws || ws_bytes < need)) return fail(MLA_ERR_WORKSPACE, "decode_attn needs %zu bytes", need);
+  if (need && !aligned16(ws)) return fail(MLA_ERR_ALIGN, "workspace not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  mla::AttnArgs a{};
+  a.q = q;
+  a.cache = cache->data;
+  a.block_table = cache->block_table;
+  a.capacity = cache->capacity;
+  a.block_size = cache->block_size;
+  a.max_blocks = cache->max_blocks;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.H = dims->H;
+  a.d_c = dims->d_c;
+  a.d_R = dims->d_R;
+  a.chunk = chunk;
+  a.splits = splits;
+  a.scale = softmax_scale(dims);
+  a.o_lat = o_lat;
+  a.lse = lse;
+  a.dtype = dims->dtype;
+  if (splits > 1) {
+    a.part_o = static_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         align_up(static_cast<size_t>(B) * splits * dims->H * dims->d_c * sizeof(float)));
+  }
+  if (max_seq_len == 0) {
+    // every sequence is empty: zeros and -inf
+    a.splits = 1;
+    a.chunk = 1;
+  }
+  if (mfma_attn(dims)) {
+    MLA_TRY(hip_status(mla::launch_attn_mfma(a, st), "attention launch"));
+  } else {
+    MLA_TRY(hip_status(mla::launch_attn_generic(a, st), "attention launch"));
+  }
+  if (a.splits > 1) MLA_TRY(hip_status(mla::launch_attn_combine(a, st), "combine launch"));
+  return ok();
+}
+
+mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat, const void* W_UV, const void* W_O,
+                        void* o_heads, void* out, void* ws, size_t ws_bytes, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
+  if (!o_lat || !W_UV || !o_heads || !ws) return fail(MLA_ERR_NULL, "out_proj: NULL pointer");
+  if ((W_O == nullptr) != (out == nullptr)) return fail(MLA_ERR_NULL, "out_proj: W_O and out must both be given or both NULL");
+  for (const void* p : {static_cast<const void*>(o_lat), W_UV, static_cast<const void*>(o_heads),
+                        static_cast<const void*>(ws)})
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "out_proj: pointer not 16-byte aligned");
+  if (W_O && (!aligned16(W_O) || !aligned16(out))) return fail(MLA_ERR_ALIGN, "out_proj: W_O/out not aligned");
+  const size_t need = ws_out(dims, B);
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "out_proj needs %zu bytes", need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = dims->dtype;
+  const bool f32 = dt == MLA_FP32;
+  const int H = dims->H, d_v = dims->d_v, d_c = dims->d_c;
+  float* P = static_cast<float*>(ws);
+  {
+    // o_heads(b,i) = W_UV(i) o_lat(b,i): per head g, A_g[b][c] = o_lat[b][g][c]
+    const GemmShape s{B, d_v, d_c, H};
+    MLA_TRY(gemm(o_lat, static_cast<long long>(H) * d_c, d_c, true, W_UV, d_c, static_cast<long long>(d_v) * d_c,
+                 false, s, dt, P, st));
+    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), H, B, d_v, o_heads,
+                                                static_cast<long long>(H) * d_v, d_v, dt, st),
+                       "reduce launch"));
+  }
+  if (W_O) {
+    const GemmShape s{B, dims->d, H * d_v, 1};
+    MLA_TRY(gemm(o_heads, static_cast<long long>(H) * d_v, 0, f32, W_O, static_cast<long long>(H) * d_v, 0, false, s,
+                 dt, P, st));
+    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), 1, B, dims->d, out, dims->d, 0, dt, st),
+                       "reduce launch"));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal declarations shared by the HIP translation units of libmla.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Scalar conversions (bf16 is carried as uint16_t bit patterns in memory).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+// Two floats -> packed bf16 pair (lo = a, hi = b), nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static __forceinline__ float ld(const float* p) { return *p; }
+  __device__ static __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static __forceinline__ float ld(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ static __forceinline__ void st(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Rotary angle cos/sin for pair j of a d_R-wide vector at integer position
+// pos: angle = pos * theta^(-2j/d_R). Evaluated in double so that long
+// contexts (angles up to ~3e4 rad) keep full float32 accuracy.
+__device__ __forceinline__ void rope_cs(int pos, int j, int d_R, float theta, float* c, float* s) {
+  double inv = pow(static_cast<double>(theta), -2.0 * j / d_R);
+  double a = static_cast<double>(pos) * inv;
+  double sd, cd;
+  sincos(a, &sd, &cd);
+  *c = static_cast<float>(cd);
+  *s = static_cast<float>(sd);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers implemented in the .hip files (all enqueue on `stream`).
+// ---------------------------------------------------------------------------
+
+// Partial-sum GEMM: P[split][g][m][n] = sum over the split's k range of
+// A_g[m][k] * W_g(n, k); W_g(n, k) = W[g*sWg + n*ldw + k] (w_kn == false) or
+// W[g*sWg + k*ldw + n] (w_kn == true). Element types by dtype.
+struct GemmArgs {
+  const void* A;  long long lda, sAg;  bool a_f32;   // A element: f32 or storage dtype
+  const void* W;  long long ldw, sWg;  bool w_kn;
+  int M, N, K, G;
+  int splits;                 // k splits (>= 1)
+  float* P;                   // [splits][G][M][N] fp32
+  int dtype;                  // storage dtype of W (and of A unless a_f32)
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// Number of k splits launch_gemm would pick for a shape (used to size workspaces).
+int gemm_splits(int M, int N, int K, int G, int dtype);
+
+// Sum the splits of P and store to a strided output in dtype out_dtype:
+// out[g*sOg + m*ldo + n] = sum_s P[s][g][m][n].
+hipError_t launch_reduce_store(const float* P, int splits, int G, int M, int N,
+                               void* out, long long ldo, long long sOg, int out_dtype,
+                               hipStream_t stream);
+// Sum splits of the rotary projection [M][G*d_R] (g = head), rotate each head's
+// d_R vector at pos[m], store to out[m*ldo + g*sOg + j].
+hipError_t launch_reduce_rope(const float* P, int splits, int M, int G, int d_R,
+                              const int32_t* pos, float theta, void* out,
+                              long long ldo, long long sOg, int out_dtype,
+                              hipStream_t stream);
+// Sum splits of the latent [M][d_c] and rotary key [M][d_R] partials,
+// optionally RMS-normalise the latent, rotate the key at pos[m], round, and
+// write the row to the cache at position pos[m].
+hipError_t launch_append(const float* Pc, int splits_c, const float* Pr, int splits_r, int M,
+                         int d_c, int d_R, const void* gamma, float eps, const int32_t* pos,
+                         float theta, const mla_cache& cache, int dtype, hipStream_t stream);
+
+// Attention. chunk = rows per split (multiple of 32 for the MFMA kernel).
+struct AttnArgs {
+  const void* q;
+  const void* cache;
+  const int32_t* block_table;
+  long long capacity;
+  int block_size, max_blocks;
+  const int32_t* seq_lens;
+  int B, H, d_c, d_R;
+  int chunk, splits;
+  float scale;
+  float* o_lat;
+  float* lse;
+  float* part_o;    // [B][splits][H][d_c]
+  float* part_ml;   // [B][splits][H][2]
+  int dtype;
+};
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,93 @@
+"""One MLA decode step on the GPU: inputs uploaded once, the four library calls.
+
+Used by the tests, the smoke check and bench.py. Holds device tensors for the
+weights, the new tokens, the latent cache and every output, plus the
+workspace the library asks for.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import mla
+from .inputs import MLAInputs
+
+
+def to_device(a: Optional[np.ndarray], dtype: str, device="cuda") -> Optional[torch.Tensor]:
+    """Stored numpy array (uint16 bf16 bits or float32) -> device tensor."""
+    if a is None:
+        return None
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+class DeviceStep:
+    def __init__(self, inp: MLAInputs, num_splits: int = 0, device="cuda"):
+        cfg = inp.cfg
+        self.cfg, self.inp, self.device = cfg, inp, device
+        self.num_splits = num_splits
+        dt = cfg.dtype
+        self.W = {k: to_device(v, dt, device) for k, v in inp.weights.items()}
+        self.h_t = to_device(inp.h_t, dt, device)
+        self.cache = to_device(inp.cache, dt, device)
+        self.block_table = (None if inp.block_table is None
+                            else torch.from_numpy(inp.block_table).to(device))
+        self.pos = torch.from_numpy(inp.ctx.astype(np.int32)).to(device)
+        self.seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(device)
+        self.max_seq_len = int(inp.seq_lens.max())
+        self.dims = mla.make_dims(cfg.d, cfg.H, cfg.d_h, cfg.d_v, cfg.d_c, cfg.d_R, cfg.d_cq, dt,
+                                  softmax_scale=cfg.scale, rope_theta=cfg.theta)
+        self.cdesc = mla.make_cache(self.cache, self.block_table)
+        B, H, D = cfg.B, cfg.H, cfg.D
+        tdt = self.dims.torch_dtype
+        self.ws = torch.empty(mla.workspace_bytes(self.dims, B, self.max_seq_len, num_splits),
+                              dtype=torch.uint8, device=device)
+        self.q = torch.empty(B, H, D, dtype=tdt, device=device)
+        self.o_lat = torch.empty(B, H, cfg.d_c, dtype=torch.float32, device=device)
+        self.lse = torch.empty(B, H, dtype=torch.float32, device=device)
+        self.o_heads = torch.empty(B, H, cfg.d_v, dtype=tdt, device=device)
+        self.out = torch.empty(B, cfg.d, dtype=tdt, device=device)
+
+    @property
+    def splits(self) -> int:
+        return mla.decode_num_splits(self.dims, self.cfg.B, self.max_seq_len, self.num_splits)
+
+    def compress_append(self):
+        mla.mla_compress_append(self.dims, self.h_t, self.W["W_DKV"], self.W["W_KR"],
+                                self.W.get("gamma_kv"), self.pos, self.cdesc, self.ws)
+
+    def absorb_q(self):
+        mla.mla_absorb_q(self.dims, self.h_t, self.W["W_DQ"], self.W["W_UQ"], self.W["W_QR"],
+                         self.W["W_UK"], self.pos, self.q, self.ws)
+
+    def decode_attn(self, num_splits: Optional[int] = None):
+        mla.mla_decode_attn(self.dims, self.q, self.cdesc, self.seq_lens, self.max_seq_len,
+                            self.o_lat, self.lse, self.ws,
+                            self.num_splits if num_splits is None else num_splits)
+
+    def out_proj(self):
+        mla.mla_out_proj(self.dims, self.o_lat, self.W["W_UV"], self.W["W_O"], self.o_heads,
+                         self.out, self.ws)
+
+    def run(self):
+        self.compress_append()
+        self.absorb_q()
+        self.decode_attn()
+        self.out_proj()
+
+    # host copies as float64 numpy
+    @staticmethod
+    def host(t: torch.Tensor) -> np.ndarray:
+        return t.detach().to(torch.float64).cpu().numpy()
+
+    def cache_row(self, b: int, u: int) -> np.ndarray:
+        if self.block_table is None:
+            return self.host(self.cache[b, u])
+        bs = self.cfg.block_size
+        blk = int(self.inp.block_table[b, u // bs])
+        return self.host(self.cache[blk, u % bs])

@@ -1,0 +1,140 @@
+"""The C-ABI library: exports, host-side validation and error codes (CPU only).
+
+Every negative case below fails validation on the host, before anything is
+enqueued, so no device pointer is ever dereferenced (the pointers passed are
+arbitrary integers chosen to be aligned or misaligned as the case needs).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_compression_mla_amd import mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED = 0, 1, 2, 3, 4, 5, 6
+
+A = 0x10000       # an aligned fake device address
+MIS = 0x10008     # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mla.lib()
+
+
+def v3(**kw):
+    args = dict(d=7168, H=128, d_h=128, d_v=128, d_c=512, d_R=64, d_cq=1536, dtype="bf16")
+    args.update(kw)
+    return mla.make_dims(**args)
+
+
+def tiny(**kw):
+    args = dict(d=256, H=4, d_h=16, d_v=16, d_c=32, d_R=8, d_cq=0, dtype="fp32")
+    args.update(kw)
+    return mla.make_dims(**args)
+
+
+def test_every_declared_entry_point_is_exported(L):
+    with open(os.path.join(ROOT, "include", "mla.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text))
+    assert {"mla_compress_append", "mla_absorb_q", "mla_decode_attn", "mla_out_proj"} <= declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(mla.EXPORTED) == declared
+
+
+def test_cache_row_bytes_match_printed_cache_size():
+    # DeepSeek-V3 geometry: (512 + 64) values x 2 bytes per layer; 61 layers
+    # give 70,272 bytes, the "about 70 KB per token" the pages quote.
+    d = v3()
+    assert mla.cache_row_bytes(d) == 1152
+    assert mla.cache_row_bytes(d) * 61 == 70272
+    assert mla.cache_row_bytes(tiny()) == 40 * 4
+
+
+def test_kernel_choice_and_split_plan():
+    assert mla.decode_kernel(v3()) == 1
+    assert mla.decode_kernel(v3(H=64)) == 1
+    assert mla.decode_kernel(v3(H=16)) == 2
+    assert mla.decode_kernel(tiny()) == 2
+    assert mla.decode_kernel(v3(d_c=256)) == 2
+    # explicit splits: equal chunks of whole 32-row tiles
+    assert mla.decode_num_splits(v3(), 64, 8193, 4) == 4
+    assert mla.decode_num_splits(v3(), 8, 32769, 32) == 32
+    assert mla.decode_num_splits(v3(), 1, 10, 50) == 1      # one 32-row tile
+    assert mla.decode_num_splits(tiny(), 1, 65, 0) >= 1
+    assert mla.workspace_bytes(v3(), 64, 8193, 1) >= 256
+    big = mla.workspace_bytes(v3(), 64, 8193, 4)
+    assert big >= 64 * 4 * 128 * 514 * 4
+
+
+def test_dims_validation(L):
+    for bad, code in ((None, NULL), (v3(dtype=7), DTYPE), (v3(d_R=63), SHAPE), (v3(H=0), SHAPE),
+                      (v3(d_cq=-1), SHAPE), (v3(rope_theta=0.0), SHAPE), (v3(d_c=2048), UNSUPPORTED),
+                      (tiny(d_c=30), ALIGN)):
+        ref = None if bad is None else ctypes.byref(bad)
+        assert L.mla_cache_row_bytes(ref) == 0
+        assert L.mla_workspace_bytes(ref, 1, 1, 0) == 0
+        st = L.mla_decode_attn(ref, 1, A, ctypes.byref(mla.MLACache(A, None, 16, 0, 0, 0)), A, 1, 0, A,
+                               None, A, 1 << 20, None)
+        assert st == code, (bad and (bad.d_R, bad.dtype), st)
+    assert L.mla_status_str(ALIGN).decode().startswith("MLA_ERR_ALIGN")
+    assert L.mla_status_str(99).decode() == "unknown mla_status"
+
+
+def test_decode_attn_argument_errors(L):
+    d = v3()
+    c = mla.MLACache(A, None, 100, 0, 0, 0)
+    call = lambda **kw: L.mla_decode_attn(
+        ctypes.byref(d), kw.get("B", 2), kw.get("q", A), ctypes.byref(kw.get("cache", c)),
+        kw.get("seq", A), kw.get("maxlen", 100), kw.get("splits", 4), kw.get("o", A), None,
+        kw.get("ws", A), kw.get("wsb", 16), None)
+    assert call(B=0) == SHAPE
+    assert call(q=None) == NULL
+    assert call(seq=None) == NULL
+    assert call(o=None) == NULL
+    assert call(q=MIS) == ALIGN
+    assert call(maxlen=101) == SHAPE                      # past the contiguous capacity
+    assert call(maxlen=-1) == SHAPE
+    assert call(splits=-2) == SHAPE
+    assert call(wsb=16) == WORKSPACE                      # 4 splits need partial buffers
+    assert call(ws=None, wsb=0) == WORKSPACE
+    assert call(cache=mla.MLACache(None, None, 100, 0, 0, 0)) == NULL
+    assert call(cache=mla.MLACache(MIS, None, 100, 0, 0, 0)) == ALIGN
+    assert call(cache=mla.MLACache(A, None, 0, 0, 0, 0)) == SHAPE
+    assert call(cache=mla.MLACache(A, A, 0, 48, 4, 10)) == UNSUPPORTED   # block size not 2^k
+    assert call(cache=mla.MLACache(A, A, 0, 64, 1, 10), maxlen=65) == SHAPE
+    assert "capacity" in L.mla_last_error().decode() or True
+
+
+def test_projection_argument_errors(L):
+    d = v3()
+    c = mla.MLACache(A, None, 100, 0, 0, 0)
+    need = L.mla_workspace_bytes(ctypes.byref(d), 4, 100, 0)
+    # compress_append
+    f = lambda h=A, wd=A, wr=A, g=None, pos=A, ws=A, wsb=need, cache=c: L.mla_compress_append(
+        ctypes.byref(d), 4, h, wd, wr, g, pos, ctypes.byref(cache), ws, wsb, None)
+    assert f(h=None) == NULL and f(wd=None) == NULL and f(pos=None) == NULL
+    assert f(wr=MIS) == ALIGN and f(g=MIS) == ALIGN
+    assert f(wsb=1) == WORKSPACE
+    # absorb_q: W_DQ must be present exactly when d_cq > 0
+    g = lambda dq=A, dims=d, wsb=need, qq=A: L.mla_absorb_q(ctypes.byref(dims), 4, A, dq, A, A, A, A, qq, A,
+                                                            wsb, None)
+    assert g(dq=None) == NULL
+    assert g(dims=v3(d_cq=0), dq=A) == NULL
+    assert g(qq=None) == NULL and g(qq=MIS) == ALIGN
+    assert g(wsb=1) == WORKSPACE
+    # out_proj: W_O and out together
+    h = lambda wo=A, out=A, wsb=need: L.mla_out_proj(ctypes.byref(d), 4, A, A, wo, A, out, A, wsb, None)
+    assert h(wo=None) == NULL and h(out=None) == NULL
+    assert h(wsb=1) == WORKSPACE
+    assert h(wo=MIS) == ALIGN
+
+
+def test_workspace_covers_every_call():
+    for dims, B, L_ in ((v3(), 64, 8193), (v3(), 8, 32769), (v3(), 128, 16385), (tiny(), 1, 65)):
+        for s in (0, 1, 2, 8):
+            assert mla.workspace_bytes(dims, B, L_, s) > 0
