@@ -25,16 +25,16 @@
 // read transposed with ds_read_b64_tr_b16 from the same row-major copy. Both
 // patterns are bank-conflict free.
 //
-// Softmax is online in base 2 (scale*log2(e) folded in) against a reference
-// maximum m_ref that only moves when a tile's maximum exceeds it by more than
-// 2^64. Below that gap the exponent's reference point simply stays (weights
-// up to 2^64 are exact in fp32/bf16 range and the final division by l removes
-// the common factor). Above it, everything accumulated so far weighs less than
-// 2^-64 per row (below 2^-49 in total for 2^15 rows) against the new maximum's
-// own row, i.e. under fp32 resolution, so the accumulation restarts from zero
-// at the new reference. The accumulator is therefore never rescaled and is
-// only ever touched by MFMA instructions: accumulate, zero (0*0 + 0) and
-// copy-out (0*0 + O), which keeps it resident in AGPRs.
+// Softmax is online in base 2 (scale*log2(e) folded in) against a fixed
+// per-head reference: the first tile's maximum. Weights exp2(x - m_ref) up to
+// 2^32 are exact in fp32/bf16 range, and the final division by l removes the
+// common factor, so no running rescale of O is needed and the accumulator is
+// only ever touched by MFMA instructions (accumulate, and zero = 0*0 + 0),
+// which keeps it resident in AGPRs. If a later tile's maximum exceeds a
+// head's reference by more than 2^32 (adversarially growing scores), the
+// workgroup redoes its chunk exactly: a scores-only pass finds every head's
+// true maximum, and a second full pass uses it as the reference (weights
+// <= 1). The result is the same softmax either way.
 //
 // Context splits: a workgroup covers rows [s*chunk, min((s+1)*chunk, L_b)).
 // With more than one split it writes unnormalised (O, m, l) partials, merged
@@ -52,10 +52,10 @@ constexpr int STAGE = LAT_BYTES + TILE * 128;   // 36 KiB
 constexpr int NSTAGE = 4;
 constexpr int NTHREADS = 256;
 constexpr int DMA_PER_WAVE = 9;       // 8 latent rows + 1 rotary block per tile
-// A tile whose maximum exceeds the reference by more than this (log2 units)
-// restarts the accumulation at the new maximum; below it the reference stays,
-// so probabilities stay in (0, 2^64].
-constexpr float RESTART_GAP = 64.0f;
+// Fast pass: a head's reference maximum is its first tile's maximum. A later
+// tile exceeding it by more than this (log2 units) sends the workgroup to the
+// exact two-pass fallback; otherwise probabilities stay in (0, 2^32].
+constexpr float REF_GAP = 32.0f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -148,12 +148,27 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint32_t st, int b, 
   dma16(mine + DC + 8 * c, st + LAT_BYTES + w * 1024);
 }
 
+// MFMA instructions issued from inline asm are invisible to the compiler's
+// hazard tracking, so each one carries its own wait states:
+//  * before it, cover a VALU write of any of its VGPR operands (the compiler
+//    may materialise or copy an operand with a VALU instruction right before);
+//  * when its result is read by the VALU next, the wait states follow it in
+//    the same asm statement, so no read can be scheduled in between.
+#define MLA_MFMA_PRE "s_nop 4\n\t"
+#define MLA_MFMA_POST "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+
+// acc = 0 * 0 + 0: clears an accumulator block through the MFMA unit.
+__device__ __forceinline__ void mfma_zero(f32x16& acc, const bf16x8& zero8) {
+  asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero8));
+}
+
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int NW, bool PAGED>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma_kernel(Params p) {
   __shared__ __align__(1024) char smem[NSTAGE * STAGE];
+  __shared__ int wg_flag;
   const uint32_t smem_lds = lds_addr(smem);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,19 +206,10 @@ void attn_mfma_kernel(Params p) {
     for (int s = 0; s < 36; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
-  // Prologue: tiles 0..NSTAGE-2 in flight. Then wait for everything issued so
-  // far (the query and these copies) so that no vector-memory wait remains
-  // pending inside the loop: the loop's waits are the explicit ones below.
-#pragma unroll
-  for (int j = 0; j < NSTAGE - 1; ++j)
-    if (j < ntiles) issue_tile<PAGED>(p, smem_lds + j * STAGE, b, row_begin + j * TILE, row_end, w, lane);
-  wait_vmcnt<0>();
-
   const bf16x8 zero8 = {};
   f32x16 oacc[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(oacc[i]) : "v"(zero8));
+  for (int i = 0; i < 16; ++i) mfma_zero(oacc[i], zero8);
   float m_ref = -INFINITY;   // reference maximum, log2 units
   float l_run = 0.f;         // this lane's partial sum (its 16 of each 32 rows)
 
@@ -232,101 +238,144 @@ void attn_mfma_kernel(Params p) {
       tr_off[k][j] = (4 * (g16 >> 1) + tr_e) * 1024 + 64 * (j ^ tr_e) + 16 * lowx + 8 * (tr_q & 1);
   }
 
-  for (int it = 0; it < ntiles; ++it) {
-    // Tile `it` was issued NSTAGE-1 iterations ago; later tiles may still fly.
-    const int later = min(ntiles - 1 - it, NSTAGE - 2);
-    if (later >= 2) wait_vmcnt<2 * DMA_PER_WAVE>();
-    else if (later == 1) wait_vmcnt<DMA_PER_WAVE>();
-    else wait_vmcnt<0>();
-    block_barrier();
-    if (it + NSTAGE - 1 < ntiles)
-      issue_tile<PAGED>(p, smem_lds + ((it + NSTAGE - 1) % NSTAGE) * STAGE, b,
-                 row_begin + (it + NSTAGE - 1) * TILE, row_end, w, lane);
-    if (!active) continue;
-
-    const char* st = smem + (it % NSTAGE) * STAGE;
-    const int nv = min(TILE, row_end - (row_begin + it * TILE));
-
-    // ---- scores: S^T[row][head] over all 576 columns ----
-    // Operand reads run two steps ahead of the MFMA that consumes them.
-    auto qk_operand = [&](int s) -> bf16x8 {
-      const char* ap = (s < 32) ? st + qk_off[s & 7] + 256 * (s >> 3) : st + rp_off[s - 32];
-      return *reinterpret_cast<const bf16x8*>(ap);
-    };
-    f32x16 sacc;
-    bf16x8 a0 = qk_operand(0), a1 = qk_operand(1);
+  // mode 0: fast pass (first-tile reference); mode 1: scores only, exact
+  // maximum (fallback); mode 2: full pass against that maximum (fallback).
+  int mode = 0;
+  for (;;) {
+    // Prologue: tiles 0..NSTAGE-2 in flight. Then wait for everything issued
+    // so far (the query and these copies) so that no vector-memory wait stays
+    // pending inside the loop: the loop's waits are the explicit ones below.
 #pragma unroll
-    for (int s = 0; s < 36; ++s) {
-      const bf16x8 a2 = (s + 2 < 36) ? qk_operand(s + 2) : a0;
-      if (s == 0) {
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(a0), "v"(qreg[s]));
-      } else {
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(a0), "v"(qreg[s]));
+    for (int j = 0; j < NSTAGE - 1; ++j)
+      if (j < ntiles) issue_tile<PAGED>(p, smem_lds + j * STAGE, b, row_begin + j * TILE, row_end, w, lane);
+    wait_vmcnt<0>();
+    bool grew = false;
+    float m_seen = -INFINITY;
+
+    for (int it = 0; it < ntiles; ++it) {
+      // Tile `it` was issued NSTAGE-1 iterations ago; later tiles may still fly.
+      const int later = min(ntiles - 1 - it, NSTAGE - 2);
+      if (later >= 2) wait_vmcnt<2 * DMA_PER_WAVE>();
+      else if (later == 1) wait_vmcnt<DMA_PER_WAVE>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      if (it + NSTAGE - 1 < ntiles)
+        issue_tile<PAGED>(p, smem_lds + ((it + NSTAGE - 1) % NSTAGE) * STAGE, b,
+                          row_begin + (it + NSTAGE - 1) * TILE, row_end, w, lane);
+      if (!active) continue;
+
+      const char* st = smem + (it % NSTAGE) * STAGE;
+      const int nv = min(TILE, row_end - (row_begin + it * TILE));
+
+      // ---- scores: S^T[row][head] over all 576 columns ----
+      // Operand reads run two steps ahead of the MFMA that consumes them.
+      auto qk_operand = [&](int s) -> bf16x8 {
+        const char* ap = (s < 32) ? st + qk_off[s & 7] + 256 * (s >> 3) : st + rp_off[s - 32];
+        return *reinterpret_cast<const bf16x8*>(ap);
+      };
+      f32x16 sacc;
+      bf16x8 a0 = qk_operand(0), a1 = qk_operand(1);
+  #pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        const bf16x8 a2 = (s + 2 < 36) ? qk_operand(s + 2) : a0;
+        if (s == 0) {
+          asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                       : "=&v"(sacc) : "v"(a0), "v"(qreg[s]));
+        } else if (s < 35) {
+          asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                       : "+v"(sacc) : "v"(a0), "v"(qreg[s]));
+        } else {
+          // last step: the softmax reads sacc next
+          asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" MLA_MFMA_POST
+                       : "+v"(sacc) : "v"(a0), "v"(qreg[s]));
+        }
+        a0 = a1;
+        a1 = a2;
       }
-      a0 = a1;
-      a1 = a2;
-    }
-    // The VALU reads the MFMA result next: the wait states are tied to sacc so
-    // that no read of it can be scheduled ahead of them.
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc));
 
-    // ---- online softmax (base 2) with a lazily moved reference max ----
-    if (nv < TILE) {
+      // ---- softmax weights (base 2) against the reference maximum ----
+      // Scores are scaled once (x = s * scale * log2 e); the maximum and the
+      // exponents use the same rounded x, so a row at the reference gets
+      // weight exactly 1.
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + 4 * h + (r & 3) >= nv) sacc[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) sacc[r] *= p.sl2;
+      if (nv < TILE) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + 4 * h + (r & 3) >= nv) sacc[r] = -INFINITY;
+      }
+      float tmax = sacc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (mode == 1) {
+        m_seen = fmaxf(m_seen, tmax);
+        continue;
+      }
+      if (mode == 0) {
+        if (it == 0) m_ref = tmax;
+        else grew = grew || (tmax > m_ref + REF_GAP);
+      }
+      float psum = 0.f;
+      float pv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pv[r] = __builtin_amdgcn_exp2f(sacc[r] - m_ref);
+        psum += pv[r];
+      }
+      l_run += psum;
+      bf16x8 pb[2];
+  #pragma unroll
+      for (int t = 0; t < 2; ++t)
+  #pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          bf16x2 v2 = __builtin_convertvector((f32x2{pv[8 * t + 2 * k], pv[8 * t + 2 * k + 1]}), bf16x2);
+          pb[t][2 * k] = v2[0];
+          pb[t][2 * k + 1] = v2[1];
+        }
+
+      // ---- O^T[col][head] += V^T P ----
+      // Transposed operand reads run one (cb, t) step ahead of their MFMA.
+      auto pv_operand = [&](int cb, int t) -> bf16x8 {
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(st + 16384 * t + 256 * (cb >> 2) + tr_off[0][cb & 3]));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(st + 16384 * t + 8192 + 256 * (cb >> 2) + tr_off[1][cb & 3]));
+        return __builtin_bit_cast(bf16x8, (s16x8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      };
+      // Steps run t-major (all 16 column blocks for rows 0-15, then rows 16-31)
+      // so that the two MFMAs into one accumulator are 16 instructions apart.
+      bf16x8 v0 = pv_operand(0, 0), v1 = pv_operand(1, 0);
+  #pragma unroll
+      for (int step = 0; step < 32; ++step) {
+        const int t = step >> 4, cb = step & 15;
+        const bf16x8 v2 = (step + 2 < 32) ? pv_operand((step + 2) & 15, (step + 2) >> 4) : v0;
+        asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+a"(oacc[cb]) : "v"(v0), "v"(pb[t]));
+        v0 = v1;
+        v1 = v2;
+      }
     }
-    float tmax = sacc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.sl2;
-    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + RESTART_GAP) != 0) {
-      // Restart at the new maximum (rare: at most a few times per chunk).
-      m_ref = fmaxf(m_ref, tmax);
+
+    if (mode == 2) break;
+    if (mode == 1) {
+      // exact maximum known: redo the chunk against it
+      m_ref = m_seen;
       l_run = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(oacc[i]) : "v"(zero8));
+      for (int i = 0; i < 16; ++i) mfma_zero(oacc[i], zero8);
+      mode = 2;
+      __syncthreads();
+      continue;
     }
-    float psum = 0.f;
-    float pv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.sl2, -m_ref));
-      psum += pv[r];
-    }
-    l_run += psum;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        bf16x2 v2 = __builtin_convertvector((f32x2{pv[8 * t + 2 * k], pv[8 * t + 2 * k + 1]}), bf16x2);
-        pb[t][2 * k] = v2[0];
-        pb[t][2 * k + 1] = v2[1];
-      }
-
-    // P was just written by the VALU and is read by MFMAs next (VALU-write to
-    // MFMA-read wait states, tied to the operands).
-    asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]));
-    // ---- O^T[col][head] += V^T P ----
-    // Transposed operand reads run one (cb, t) step ahead of their MFMA.
-    auto pv_operand = [&](int cb, int t) -> bf16x8 {
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(st + 16384 * t + 256 * (cb >> 2) + tr_off[0][cb & 3]));
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(st + 16384 * t + 8192 + 256 * (cb >> 2) + tr_off[1][cb & 3]));
-      return __builtin_bit_cast(bf16x8, (s16x8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-    };
-    bf16x8 v0 = pv_operand(0, 0), v1 = pv_operand(0, 1);
-#pragma unroll
-    for (int step = 0; step < 32; ++step) {
-      const int cb = step >> 1, t = step & 1;
-      const bf16x8 v2 = (step + 2 < 32) ? pv_operand((step + 2) >> 1, (step + 2) & 1) : v0;
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(oacc[cb]) : "v"(v0), "v"(pb[t]));
-      v0 = v1;
-      v1 = v2;
-    }
+    // mode 0 done: did any head in the workgroup outgrow its reference?
+    if (tid == 0) wg_flag = 0;
+    __syncthreads();
+    if (active && __builtin_amdgcn_ballot_w64(grew) != 0 && lane == 0) wg_flag = 1;
+    __syncthreads();
+    if (wg_flag == 0) break;
+    mode = 1;
+    __syncthreads();
   }
 
   if (!active) return;

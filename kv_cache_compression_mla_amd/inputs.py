@@ -33,7 +33,7 @@ BF16_NAN = np.uint16(0x7FC0)
 # Order in which child random streams are spawned from the seed. Fixed so that
 # every consumer draws identical values.
 _STREAMS = ("W_DKV", "W_KR", "W_DQ", "W_UQ", "W_QR", "W_UK", "W_UV", "W_O",
-            "h_t", "history", "ctx", "pages", "gamma")
+            "h_t", "history", "ctx", "pages", "gamma", "q")
 
 
 @dataclass(frozen=True)
@@ -242,3 +242,10 @@ def make_inputs(cfg: MLAConfig, with_weights: bool = True) -> MLAInputs:
             if rem:
                 pool[table[b, full], :rem] = rows[full * bs:]
     return MLAInputs(cfg, weights, h_t, ctx, seq_lens, pool, table, 0)
+
+
+def make_query(cfg: MLAConfig, q_std: float = 0.5) -> np.ndarray:
+    """A seeded absorbed query [B][H][d_c + d_R] in the storage dtype, for
+    exercising the attention call on its own (default std gives scores of
+    about the spread a full V3-shaped step produces)."""
+    return _draw(_rngs(cfg.seed)["q"], (cfg.B, cfg.H, cfg.D), q_std, cfg.dtype)

@@ -27,7 +27,8 @@ def to_device(a: Optional[np.ndarray], dtype: str, device="cuda") -> Optional[to
 
 
 class DeviceStep:
-    def __init__(self, inp: MLAInputs, num_splits: int = 0, device="cuda"):
+    def __init__(self, inp: MLAInputs, num_splits: int = 0, device="cuda", ws_splits=()):
+        """ws_splits: further split counts the workspace must also cover."""
         cfg = inp.cfg
         self.cfg, self.inp, self.device = cfg, inp, device
         self.num_splits = num_splits
@@ -45,8 +46,9 @@ class DeviceStep:
         self.cdesc = mla.make_cache(self.cache, self.block_table)
         B, H, D = cfg.B, cfg.H, cfg.D
         tdt = self.dims.torch_dtype
-        self.ws = torch.empty(mla.workspace_bytes(self.dims, B, self.max_seq_len, num_splits),
-                              dtype=torch.uint8, device=device)
+        ws_bytes = max(mla.workspace_bytes(self.dims, B, self.max_seq_len, s)
+                       for s in (num_splits, *ws_splits))
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         self.q = torch.empty(B, H, D, dtype=tdt, device=device)
         self.o_lat = torch.empty(B, H, cfg.d_c, dtype=torch.float32, device=device)
         self.lse = torch.empty(B, H, dtype=torch.float32, device=device)

@@ -152,7 +152,7 @@ def test_single_row_context_returns_stored_latent_exactly():
 def test_splits_are_an_exact_reformulation_and_deterministic():
     cfg = V3.with_(name="v3_splits", B=2, ctx=(700, 1500), seed=9)
     inp = make_inputs(cfg)
-    st = DeviceStep(inp, num_splits=1)
+    st = DeviceStep(inp, num_splits=1, ws_splits=(2, 3, 7, 0))
     st.compress_append()
     st.absorb_q()
     outs = {}
@@ -164,10 +164,18 @@ def test_splits_are_an_exact_reformulation_and_deterministic():
         st.decode_attn(num_splits=s)
         torch.cuda.synchronize()
         assert np.array_equal(outs[s][0], st.host(st.o_lat)), f"non-deterministic at splits={s}"
-    ref = outs[1][0]
+    # Mathematically the split count changes nothing; numerically each split
+    # rounds its probabilities to bf16 against its own maximum, so results
+    # agree to the bf16 parity bar and every split count meets it against
+    # the oracle.
+    W = weights64(inp)
+    refs = [oracle_seq(inp, W, b, unabsorbed=False)["abs"] for b in range(cfg.B)]
     for s, (o, l) in outs.items():
-        assert rel_err(o, ref) <= 2e-3, s       # bf16 P per split tile order; fp32 sums
-        assert np.abs(l - outs[1][1]).max() <= 1e-3 * np.abs(outs[1][1]).max()
+        e_split = rel_err(o, outs[1][0])
+        e_lse = np.abs(l - outs[1][1]).max() / np.abs(outs[1][1]).max()
+        e_ref = max(rel_err(o[b], refs[b]["o_lat"]) for b in range(cfg.B))
+        say(f"splits={s}: vs 1 split {e_split:.2e} (lse {e_lse:.2e}); vs oracle {e_ref:.2e}")
+        assert e_split <= 1e-2 and e_ref <= 1e-2 and e_lse <= 1e-4, s
 
 
 def test_paged_equals_contiguous_bitwise():
@@ -190,25 +198,69 @@ def test_paged_equals_contiguous_bitwise():
     assert np.array_equal(outs[0][1], outs[1][1])
 
 
-def test_growing_scores_restart_path():
-    """Scores that grow by far more than 2^64 across the context exercise the
-    kernel's restart of the running sums at a new maximum."""
-    cfg = V3.with_(name="v3_growing", B=1, ctx=(400,), seed=13)
-    inp = make_inputs(cfg)
-    rows = gen.to_f64(inp.cache[0, :400], "bf16")
-    # make later rows increasingly aligned with a fixed direction of the latent
-    # and scale them up: scores then climb steeply with the row index
-    scale = np.linspace(0.1, 25.0, 400)[:, None]
-    rows = rows * scale
-    inp.cache[0, :400] = gen.f32_to_bf16_bits(rows.astype(np.float32))
-    st = DeviceStep(inp, num_splits=1)
-    st.run()
+def fill_append_slots(inp):
+    """Give the row at each sequence's append position a value (attention
+    alone reads seq_lens = ctx + 1 rows and no append runs)."""
+    rng = np.random.default_rng(1234)
+    for b in range(inp.cfg.B):
+        v = (rng.standard_normal(inp.cfg.D) * 1.7).astype(np.float32)
+        inp.row(b, int(inp.ctx[b]))[:] = gen.f32_to_bf16_bits(v)
+
+
+def attention_only(inp, q_bits, num_splits):
+    """Run mla_decode_attn alone on a generator-made query."""
+    st = DeviceStep(inp, num_splits=num_splits)
+    from kv_cache_compression_mla_amd.step import to_device
+    q = to_device(q_bits, inp.cfg.dtype)
+    mla.mla_decode_attn(st.dims, q, st.cdesc, st.seq_lens, st.max_seq_len, st.o_lat, st.lse, st.ws,
+                        num_splits)
     torch.cuda.synchronize()
-    W = weights64(inp)
-    r = oracle_seq(inp, W, 0)
-    s_max = (r["abs"]["lse"] * 1.4426950408889634).max()
-    say(f"growing: max lse(log2)={s_max:.1f}")
-    check_step(inp, st, label="growing")
+    return st
+
+
+def check_attention(inp, st, q_bits, label, seqs=None):
+    cfg = inp.cfg
+    q64 = gen.to_f64(q_bits, cfg.dtype)
+    o_lat, lse = st.host(st.o_lat), st.host(st.lse)
+    for b in (range(cfg.B) if seqs is None else seqs):
+        n = int(inp.seq_lens[b])
+        rows = gen.to_f64(inp.rows(b, n), cfg.dtype)   # attention alone: no append
+        ref_o, ref_l = om.attend_absorbed(q64[b, :, :cfg.d_c], q64[b, :, cfg.d_c:], rows, cfg.scale)
+        e_o = rel_err(o_lat[b], ref_o)
+        e_l = np.abs(lse[b] - ref_l).max() / max(np.abs(ref_l).max(), 1.0)
+        say(f"{label} b={b} L={n} o_lat {e_o:.2e} lse {e_l:.2e}")
+        assert e_o <= tol(cfg) and e_l <= tol(cfg), (label, b, e_o, e_l)
+
+
+def test_growing_scores_take_the_exact_fallback():
+    """Scores that grow by far more than 2^32 over the context (later rows
+    scaled up) send the kernel to its exact two-pass path; the result still
+    matches the oracle. The query comes from the generator, so both sides
+    see identical bf16 inputs."""
+    cfg = V3.with_(name="v3_growing", B=2, ctx=(399, 1000), seed=13)
+    inp = make_inputs(cfg)
+    fill_append_slots(inp)
+    for b in range(cfg.B):
+        n = int(inp.seq_lens[b])
+        rows = gen.to_f64(inp.cache[b, :n], "bf16")
+        scale = np.linspace(0.1, 12.0, n)[:, None]
+        inp.cache[b, :n] = gen.f32_to_bf16_bits((rows * scale).astype(np.float32))
+    q = gen.make_query(cfg)
+    for splits in (1, 3):
+        st = attention_only(inp, q, splits)
+        lse2 = st.host(st.lse) * 1.4426950408889634
+        say(f"growing splits={splits}: lse range (log2) {lse2.min():.1f}..{lse2.max():.1f}")
+        check_attention(inp, st, q, f"growing s={splits}")
+
+
+def test_attention_alone_against_oracle():
+    cfg = V3.with_(name="v3_attn", B=3, ctx=(0, 700, 2500), seed=21)
+    inp = make_inputs(cfg)
+    q = gen.make_query(cfg)
+    fill_append_slots(inp)
+    for splits in (1, 4, 0):
+        st = attention_only(inp, q, splits)
+        check_attention(inp, st, q, f"attn s={splits}")
 
 
 @pytest.mark.parametrize("name,seqs,unabs", [
