@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""MLA decode benchmark on one MI355X.
+
+One step = the whole decode hot path over one batch: compress + RoPE + append
+of the new tokens, absorbed query, latent-space attention against the cache
+(with the cross-split combine), and the output projections. Inputs are seeded
+synthetic tensors of the DeepSeek-V3 geometry, resident in HBM before timing.
+
+Headline: decode-attention TFLOP/s (algorithmic FLOPs 2*H*(D + d_c) per
+attended row) and latent-cache GB/s (1152 B per attended row) of the
+mla_decode_attn call, both from HIP events recorded on the stream the library
+launches on; ms_per_step is the whole step. The roofline object prices the
+attention call against MI355X's published HBM bandwidth (8 TB/s); the CPU
+baseline times the float64 oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+ATTN_SRC = os.path.join(ROOT, "kv_cache_compression_mla_amd", "csrc", "attn_mfma.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attn_work(cfg, seq_lens):
+    """Algorithmic bytes and FLOPs of one mla_decode_attn call."""
+    rows = int(seq_lens.sum())
+    row_bytes = cfg.D * 2
+    cache_bytes = rows * row_bytes
+    q_bytes = cfg.B * cfg.H * cfg.D * 2
+    out_bytes = cfg.B * cfg.H * cfg.d_c * 4 + cfg.B * cfg.H * 4
+    flops = rows * 2 * cfg.H * (cfg.D + cfg.d_c)
+    return rows, cache_bytes, cache_bytes + q_bytes + out_bytes, flops
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per attention call from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            prof = json.load(f)
+        with open(ATTN_SRC, "rb") as f:
+            src_hash = hashlib.sha256(f.read()).hexdigest()
+        if prof.get("attn_source_sha256") != src_hash:
+            return None
+        return prof.get("bytes_per_call")
+    except Exception:
+        return None
+
+
+def cpu_baseline(inp, budget_s):
+    """Time the float64 oracle (unabsorbed: per-head K and V rebuilt from every
+    cached latent) on whole sequences of the workload until the budget is used."""
+    import numpy as np
+    from kv_cache_compression_mla_amd import inputs as gen
+    from oracle import mla_oracle as om
+    cfg = inp.cfg
+    cores = len(os.sched_getaffinity(0))
+    W = {k: (None if v is None else gen.to_f64(v, cfg.dtype)) for k, v in inp.weights.items()}
+    done_rows, t_used, nseq = 0, 0.0, 0
+    for b in range(cfg.B):
+        h = gen.to_f64(inp.h_t[b], cfg.dtype)
+        prior = gen.to_f64(inp.rows(b, int(inp.ctx[b])), cfg.dtype)
+        t0 = time.perf_counter()
+        om.decode_step(h, prior, W, int(inp.ctx[b]), cfg.theta, cfg.scale, cfg.dtype)
+        t_used += time.perf_counter() - t0
+        done_rows += int(inp.seq_lens[b])
+        nseq += 1
+        if t_used >= budget_s:
+            break
+    flops = done_rows * 2 * cfg.H * (cfg.D + cfg.d_c)
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nseq} of {cfg.B} sequences ({done_rows} attended rows, all {cfg.H} heads), "
+                      f"float64 numpy unabsorbed step, {t_used:.1f} s; value counts the same "
+                      f"algorithmic attention FLOPs as the GPU line"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v3_b64_ctx8k")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path is "
+              "single-GPU in this build. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from kv_cache_compression_mla_amd import inputs as gen
+    from kv_cache_compression_mla_amd import mla
+    from kv_cache_compression_mla_amd.step import DeviceStep
+
+    if not os.path.exists(mla.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = gen.CONFIGS[args.workload]
+    t0 = time.perf_counter()
+    inp = gen.make_inputs(cfg)
+    log(f"inputs for {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
+    st = DeviceStep(inp, num_splits=args.num_splits)
+    rows, cache_bytes, attn_bytes, attn_flops = attn_work(cfg, inp.seq_lens)
+    splits = st.splits
+    log(f"B={cfg.B} rows={rows} splits={splits} kernel={mla.decode_kernel(st.dims)}")
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        st.compress_append()
+        st.absorb_q()
+        ev[k][0].record(stream)
+        st.decode_attn()
+        ev[k][1].record(stream)
+        st.out_proj()
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = t_total * 1e3 / args.steps
+
+    tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    cache_gbps = cache_bytes / (attn_ms * 1e-3) / 1e9
+    achieved_gbps = attn_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(cfg.name)
+    result = {
+        "metric": "MLA decode-attn TFLOP/s + cache GB/s (% roofline), H=128 d_c=512+64, bs64 ctx8K",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.B, "ctx": int(inp.ctx.max()),
+                   "rows_attended": rows, "heads": cfg.H, "d_c": cfg.d_c, "d_R": cfg.d_R,
+                   "paged": cfg.paged, "num_splits": splits},
+        "attn_ms": round(attn_ms, 5),
+        "cache_GBps": round(cache_gbps, 1),
+        "pct_hbm_roofline": round(100 * achieved_gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "mla_decode_attn call (attn_mfma_kernel + attn_combine_kernel)",
+                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
