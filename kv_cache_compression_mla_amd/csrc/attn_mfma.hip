@@ -14,16 +14,21 @@
 //   O^T[col][head] += V_tile^T[col][rows] . P[rows][head]      (MFMA 32x32x16)
 // with V_tile = K_tile[:, 0:512]. A wave keeps its query block (32 heads x
 // 576, bf16) in VGPRs and its O^T accumulator (512 x 32 fp32) in AGPRs for
-// the whole chunk.
+// the whole chunk. The score contraction runs as two interleaved
+// accumulation chains (even and odd 16-column steps) so that consecutive
+// MFMAs are independent.
 //
 // Memory path: each 32-row tile is copied HBM -> LDS once per workgroup by
-// LDS-DMA (global_load_lds, 16 B per lane), four stages deep, so nothing is
-// staged in registers. In LDS the latent part is row-major (1 KiB per row)
-// with 16-byte chunks XOR-swizzled per row, the rotary part is packed 128 B
-// per row with its own swizzle. The score operand is read with ds_read_b128
-// (lanes walk rows); the value operand, whose reduction index is the row, is
-// read transposed with ds_read_b64_tr_b16 from the same row-major copy. Both
-// patterns are bank-conflict free.
+// LDS-DMA (global_load_lds, 16 B per lane, one 1 KiB row latent per copy),
+// four stages deep, so nothing is staged in registers. In LDS the latent
+// rows sit at a 1040-byte stride and the rotary parts are packed 128 B per
+// row with an XOR swizzle of their 16-byte chunks. The score operand is read
+// with ds_read_b128 (lanes walk rows); the value operand, whose reduction
+// index is the row, is read transposed with ds_read_b64_tr_b16 from the same
+// row-major copy. A value block of 32 columns covers four runs of 8 columns
+// 32 apart, which makes the transposed reads of 32 lanes tile all 64 banks;
+// both read patterns are bank-conflict free and every address is one
+// per-lane base plus a compile-time offset.
 //
 // Softmax is online in base 2 (scale*log2(e) folded in) against a fixed
 // per-head reference: the first tile's maximum. Weights exp2(x - m_ref) up to
@@ -47,8 +52,9 @@ namespace {
 constexpr int DC = 512;               // latent width
 constexpr int DW = 576;               // row width (latent + rotary key)
 constexpr int TILE = 32;              // rows per stage
-constexpr int LAT_BYTES = TILE * 1024;
-constexpr int STAGE = LAT_BYTES + TILE * 128;   // 36 KiB
+constexpr int LROW = 1040;            // LDS stride of a latent row (1024 + 16)
+constexpr int LAT_BYTES = TILE * LROW;          // 33280
+constexpr int STAGE = LAT_BYTES + TILE * 128;   // 37376
 constexpr int NSTAGE = 4;
 constexpr int NTHREADS = 256;
 constexpr int DMA_PER_WAVE = 9;       // 8 latent rows + 1 rotary block per tile
@@ -61,7 +67,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct Params {
@@ -79,11 +84,13 @@ struct Params {
   float* part_ml;
 };
 
-// Swizzle of the 16-byte chunk position inside a latent row (a bijection of
-// the low 4 bits): conflict-free for 16 lanes reading 16 rows of one chunk and
-// for 32 lanes transposed-reading 4 rows x 32 columns.
-__device__ __forceinline__ int lat_sw(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+// XOR swizzle of the 16-byte chunks of a packed 128-byte rotary row: 16
+// lanes reading one chunk of 16 rows hit distinct bank groups.
 __device__ __forceinline__ int rope_sw(int r) { return (r >> 1) & 7; }
+
+// First column of value block cb: blocks hold columns
+// colbase + {0..7} + 32 * {0..3}.
+__host__ __device__ constexpr int colbase(int cb) { return 8 * (cb % 4) + 128 * (cb / 4); }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
 // [15:14], expcnt[6:4], lgkmcnt[11:8]; unconstrained fields at maximum).
@@ -123,10 +130,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
 }
 
-// Issue this wave's 9 LDS-DMA copies of tile rows [r0, r0+32) into stage
-// buffer at LDS address `st`: latent parts of rows 8w..8w+7 (1 KiB each) and
-// the rotary parts of the same 8 rows (128 B each, one copy). Rows at or past
-// row_end are replaced by row_end-1 (a real row, later masked out of the
+// Issue this wave's 9 LDS-DMA copies of tile rows [r0, r0+32) into the stage
+// at LDS address `st`: the latents of rows 8w..8w+7 (1 KiB each, straight)
+// and the rotary parts of the same 8 rows (128 B each, one copy). Rows at or
+// past row_end are replaced by row_end-1 (a real row, later masked out of the
 // softmax), so no invalid address is ever read. w, r0, row_end are uniform.
 template <bool PAGED>
 __device__ __forceinline__ void issue_tile(const Params& p, uint32_t st, int b, int r0, int row_end,
@@ -135,10 +142,7 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint32_t st, int b, 
 #pragma unroll
   for (int k = 0; k < 8; ++k) rp[k] = row_ptr<PAGED>(p, b, min(r0 + 8 * w + k, row_end - 1));
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int r = 8 * w + k;
-    dma16(rp[k] + 8 * (lane ^ lat_sw(r)), st + r * 1024);
-  }
+  for (int k = 0; k < 8; ++k) dma16(rp[k] + 8 * lane, st + (8 * w + k) * LROW);
   // rotary block: lane -> row 8w + (lane >> 3), chunk (lane & 7) ^ rope_sw(row)
   const int j = lane >> 3;
   const uint16_t* mine = rp[0];
@@ -148,12 +152,16 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint32_t st, int b, 
   dma16(mine + DC + 8 * c, st + LAT_BYTES + w * 1024);
 }
 
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // MFMA instructions issued from inline asm are invisible to the compiler's
-// hazard tracking, so each one carries its own wait states:
-//  * before it, cover a VALU write of any of its VGPR operands (the compiler
-//    may materialise or copy an operand with a VALU instruction right before);
-//  * when its result is read by the VALU next, the wait states follow it in
-//    the same asm statement, so no read can be scheduled in between.
+// hazard tracking. Where an operand is produced by the VALU (the zero
+// operand, the packed probabilities) the asm carries the VALU-write to
+// MFMA-read wait states itself; where the VALU reads an MFMA result next, the
+// wait states follow the MFMA inside the same asm statement, so no read can
+// be scheduled in between. All other operands come from memory loads, whose
+// completion the compiler's counter waits cover; a CPU test scans the
+// compiled ISA for every VALU write close before an MFMA that reads it.
 #define MLA_MFMA_PRE "s_nop 4\n\t"
 #define MLA_MFMA_POST "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
 
@@ -161,8 +169,6 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint32_t st, int b, 
 __device__ __forceinline__ void mfma_zero(f32x16& acc, const bf16x8& zero8) {
   asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero8));
 }
-
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int NW, bool PAGED>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -213,30 +219,17 @@ void attn_mfma_kernel(Params p) {
   float m_ref = -INFINITY;   // reference maximum, log2 units
   float l_run = 0.f;         // this lane's partial sum (its 16 of each 32 rows)
 
-  // Per-lane LDS byte offsets inside a stage; everything that varies with the
-  // unrolled loop indices below is a compile-time immediate on top of these.
-  // Score operand (lanes = rows): latent chunk c = 2s + h of row l32 sits at
-  // 16 * ((c & ~15) | ((c & 15) ^ lat_sw(l32))).
-  int qk_off[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) qk_off[j] = l32 * 1024 + 16 * ((2 * j + h) ^ lat_sw(l32));
-  int rp_off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) rp_off[j] = LAT_BYTES + l32 * 128 + 16 * ((2 * j + h) ^ rope_sw(l32));
-  // Value operand, transposed read: in its 16-lane group a lane supplies row
-  // r = 16t + 8k + 4*(g16>>1) + tr_e and columns col = 32cb + 16*(g16&1) + 4*tr_q.
-  // With lat_sw(r) = 4*tr_e + ((2k + (g16>>1)) & 3) the swizzled address is
-  // 16384t + 8192k + 256*(cb>>2) + tr_off[k][cb&3].
+  // Per-lane LDS bases inside a stage; every other part of an operand address
+  // is a compile-time immediate of the unrolled loops below.
+  //  score operand: row l32, latent chunk 2s + h at 16 * (2s + h)
+  const int qk_base = l32 * LROW + 16 * h;
+  //  rotary part of row l32: chunk c' at 16 * (c' ^ rope_sw(l32))
+  const int rp_base = LAT_BYTES + l32 * 128;
+  const int rp_sw = rope_sw(l32);
+  //  value operand, transposed read: in its 16-lane group a lane supplies row
+  //  16t + 8k + 4*(g16>>1) + tr_e, 8 bytes at column colbase(cb) + 32*tr_q + 4*(g16&1)
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int tr_e = i16 >> 2, tr_q = i16 & 3;
-  int tr_off[2][4];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int lowx = (2 * (g16 & 1) + (tr_q >> 1)) ^ ((2 * k + (g16 >> 1)) & 3);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      tr_off[k][j] = (4 * (g16 >> 1) + tr_e) * 1024 + 64 * (j ^ tr_e) + 16 * lowx + 8 * (tr_q & 1);
-  }
+  const int tr_base = (4 * (g16 >> 1) + (i16 >> 2)) * LROW + 64 * (i16 & 3) + 8 * (g16 & 1);
 
   // mode 0: fast pass (first-tile reference); mode 1: scores only, exact
   // maximum (fallback); mode 2: full pass against that maximum (fallback).
@@ -268,37 +261,42 @@ void attn_mfma_kernel(Params p) {
       const int nv = min(TILE, row_end - (row_begin + it * TILE));
 
       // ---- scores: S^T[row][head] over all 576 columns ----
-      // Operand reads run two steps ahead of the MFMA that consumes them.
+      // Two accumulation chains (even / odd steps); operand reads run two
+      // steps ahead of the MFMA that consumes them.
       auto qk_operand = [&](int s) -> bf16x8 {
-        const char* ap = (s < 32) ? st + qk_off[s & 7] + 256 * (s >> 3) : st + rp_off[s - 32];
+        const char* ap = (s < 32) ? st + qk_base + 32 * s
+                                  : st + rp_base + 16 * ((2 * (s - 32) + h) ^ rp_sw);
         return *reinterpret_cast<const bf16x8*>(ap);
       };
-      f32x16 sacc;
+      f32x16 sacc0, sacc1;
       bf16x8 a0 = qk_operand(0), a1 = qk_operand(1);
-  #pragma unroll
+#pragma unroll
       for (int s = 0; s < 36; ++s) {
         const bf16x8 a2 = (s + 2 < 36) ? qk_operand(s + 2) : a0;
         if (s == 0) {
-          asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                       : "=&v"(sacc) : "v"(a0), "v"(qreg[s]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc0) : "v"(a0), "v"(qreg[s]));
+        } else if (s == 1) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc1) : "v"(a0), "v"(qreg[s]));
         } else if (s < 35) {
-          asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                       : "+v"(sacc) : "v"(a0), "v"(qreg[s]));
+          if (s & 1)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc1) : "v"(a0), "v"(qreg[s]));
+          else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc0) : "v"(a0), "v"(qreg[s]));
         } else {
-          // last step: the softmax reads sacc next
-          asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" MLA_MFMA_POST
-                       : "+v"(sacc) : "v"(a0), "v"(qreg[s]));
+          // last step: the VALU reads both chains next
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0" MLA_MFMA_POST
+                       : "+v"(sacc1), "+v"(sacc0) : "v"(a0), "v"(qreg[s]));
         }
         a0 = a1;
         a1 = a2;
       }
+      f32x16 sacc = sacc0 + sacc1;
 
       // ---- softmax weights (base 2) against the reference maximum ----
       // Scores are scaled once (x = s * scale * log2 e); the maximum and the
       // exponents use the same rounded x, so a row at the reference gets
       // weight exactly 1.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] *= p.sl2;
+      sacc *= p.sl2;
       if (nv < TILE) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -317,41 +315,41 @@ void attn_mfma_kernel(Params p) {
         else grew = grew || (tmax > m_ref + REF_GAP);
       }
       float psum = 0.f;
-      float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(sacc[r] - m_ref);
-        psum += pv[r];
+        sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - m_ref);
+        psum += sacc[r];
       }
       l_run += psum;
       bf16x8 pb[2];
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < 2; ++t)
-  #pragma unroll
+#pragma unroll
         for (int k = 0; k < 4; ++k) {
-          bf16x2 v2 = __builtin_convertvector((f32x2{pv[8 * t + 2 * k], pv[8 * t + 2 * k + 1]}), bf16x2);
+          bf16x2 v2 = __builtin_convertvector((f32x2{sacc[8 * t + 2 * k], sacc[8 * t + 2 * k + 1]}), bf16x2);
           pb[t][2 * k] = v2[0];
           pb[t][2 * k + 1] = v2[1];
         }
+      // P was just written by the VALU and is read by MFMAs next (VALU-write
+      // to MFMA-read wait states, tied to the operands).
+      asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]));
 
       // ---- O^T[col][head] += V^T P ----
-      // Transposed operand reads run one (cb, t) step ahead of their MFMA.
+      // Steps run t-major (all 16 column blocks for rows 0-15, then rows
+      // 16-31) so that the two MFMAs into one accumulator are 16 apart; the
+      // transposed operand reads run two steps ahead.
       auto pv_operand = [&](int cb, int t) -> bf16x8 {
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(st + 16384 * t + 256 * (cb >> 2) + tr_off[0][cb & 3]));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(st + 16384 * t + 8192 + 256 * (cb >> 2) + tr_off[1][cb & 3]));
+        const char* a = st + tr_base + (16 * LROW) * t + 2 * colbase(cb);
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * LROW));
         return __builtin_bit_cast(bf16x8, (s16x8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
       };
-      // Steps run t-major (all 16 column blocks for rows 0-15, then rows 16-31)
-      // so that the two MFMAs into one accumulator are 16 instructions apart.
       bf16x8 v0 = pv_operand(0, 0), v1 = pv_operand(1, 0);
-  #pragma unroll
+#pragma unroll
       for (int step = 0; step < 32; ++step) {
         const int t = step >> 4, cb = step & 15;
         const bf16x8 v2 = (step + 2 < 32) ? pv_operand((step + 2) & 15, (step + 2) >> 4) : v0;
-        asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                     : "+a"(oacc[cb]) : "v"(v0), "v"(pb[t]));
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(oacc[cb]) : "v"(v0), "v"(pb[t]));
         v0 = v1;
         v1 = v2;
       }
@@ -386,16 +384,19 @@ void attn_mfma_kernel(Params p) {
   float* o = (p.splits == 1)
                  ? p.o_lat + (static_cast<long long>(b) * p.H + head) * DC
                  : p.part_o + ((static_cast<long long>(b) * p.splits + s_idx) * p.H + head) * DC;
-  o += 4 * h;
+  // D[i][head] of block cb holds column colbase(cb) + 32*((i&15)>>2) + 4*(i>>4) + (i&3);
+  // register 4g + m of this lane is i = 8g + 4h + m.
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) {
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[cb][r]));
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<f32x4*>(o + 32 * cb + 8 * g) =
+    for (int g = 0; g < 4; ++g) {
+      const int col = colbase(cb) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
+      *reinterpret_cast<f32x4*>(o + col) =
           f32x4{x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv};
+    }
   }
   if (h == 0) {
     if (p.splits == 1) {
