@@ -8,27 +8,41 @@
 // flow": content and rotary dot products summed, softmax over all history).
 //
 // Work decomposition: one workgroup = one sequence x one context chunk x all
-// H heads, one wave per 32 heads. The heads that share a latent row form a
-// dense contraction:
+// H heads, four waves. The heads that share a latent row form two dense
+// contractions per 32-row tile:
 //   S^T[row][head] = K_tile[row][0:576] . Q^T[0:576][head]     (MFMA 32x32x16)
 //   O^T[col][head] += V_tile^T[col][rows] . P[rows][head]      (MFMA 32x32x16)
-// with V_tile = K_tile[:, 0:512]. A wave keeps its query block (32 heads x
-// 576, bf16) in VGPRs and its O^T accumulator (512 x 32 fp32) in AGPRs for
-// the whole chunk. The score contraction runs as two interleaved
-// accumulation chains (even and odd 16-column steps) so that consecutive
-// MFMAs are independent.
+// with V_tile = K_tile[:, 0:512]. The score side is split by heads: wave w
+// keeps the query block of heads 32w..32w+31 (32 x 576 bf16) in VGPRs, and
+// computes their scores and softmax weights. The value side is split by
+// latent columns: wave w accumulates O^T for columns 128w..128w+127 of all
+// H heads (128 x 128 fp32 in AGPRs). The weights cross between the two
+// splits through a small LDS buffer (bf16, 64 B per head per tile). Split
+// this way, each wave reads only its quarter of V with transposed reads, 4x
+// fewer than a head split, which is what bounds the value phase.
 //
 // Memory path: each 32-row tile is copied HBM -> LDS once per workgroup by
-// LDS-DMA (global_load_lds, 16 B per lane, one 1 KiB row latent per copy),
-// four stages deep, so nothing is staged in registers. In LDS the latent
-// rows sit at a 1040-byte stride and the rotary parts are packed 128 B per
-// row with an XOR swizzle of their 16-byte chunks. The score operand is read
-// with ds_read_b128 (lanes walk rows); the value operand, whose reduction
-// index is the row, is read transposed with ds_read_b64_tr_b16 from the same
-// row-major copy. A value block of 32 columns covers four runs of 8 columns
-// 32 apart, which makes the transposed reads of 32 lanes tile all 64 banks;
-// both read patterns are bank-conflict free and every address is one
-// per-lane base plus a compile-time offset.
+// LDS-DMA (global_load_lds, 16 B per lane: one copy moves one 1 KiB row
+// latent, or the 128 B rotary parts of 8 rows), so nothing is staged in
+// registers. Row addresses are wave-uniform (scalar base + per-lane offset),
+// so a paged cache costs one scalar table read per 8 rows. LDS holds four
+// latent stages (rows at a 1040-byte stride), three rotary slots (a tile's
+// rotary part is dead once its scores are done; 128 B per row, 16-byte
+// chunks XOR-swizzled) and two weight buffers (head records of four 16-byte
+// slots, XOR-swizzled). The score operand is read with ds_read_b128 (lanes
+// walk rows); the value operand, whose reduction index is the row, is read
+// transposed with ds_read_b64_tr_b16 from the same row-major copy. A value
+// block of 32 columns covers four runs of 8 columns 32 apart, which makes
+// the transposed reads of 32 lanes tile all 64 banks. All three read
+// patterns are bank-conflict free and every address is one per-lane base
+// plus a compile-time offset.
+//
+// Software pipeline (one wave per SIMD): iteration t runs the score MFMAs of
+// tile t+1 with this wave's nine LDS-DMA copies of tile t+3 slotted between
+// them, then the value MFMAs of tile t with the softmax of tile t+1 slotted
+// between those (its weights go to the other weight buffer). One barrier per
+// tile publishes the copies of tile t+1 and the weights of tile t, and frees
+// the stages of tile t-1 for tile t+3.
 //
 // Softmax is online in base 2 (scale*log2(e) folded in) against a fixed
 // per-head reference: the first tile's maximum. Weights exp2(x - m_ref) up to
@@ -51,17 +65,35 @@ namespace {
 
 constexpr int DC = 512;               // latent width
 constexpr int DW = 576;               // row width (latent + rotary key)
+constexpr int ROW_BYTES = 2 * DW;     // 1152
 constexpr int TILE = 32;              // rows per stage
-constexpr int LROW = 1040;            // LDS stride of a latent row (1024 + 16)
-constexpr int LAT_BYTES = TILE * LROW;          // 33280
-constexpr int STAGE = LAT_BYTES + TILE * 128;   // 37376
-constexpr int NSTAGE = 4;
 constexpr int NTHREADS = 256;
 constexpr int DMA_PER_WAVE = 9;       // 8 latent rows + 1 rotary block per tile
+constexpr int QK_STEPS = DW / 16;     // 36 score MFMAs per tile
+constexpr int QK_DIST = 4;            // score-operand reads in flight
+constexpr int PV_DIST = 3;            // value operands (pairs of reads) in flight
 // Fast pass: a head's reference maximum is its first tile's maximum. A later
 // tile exceeding it by more than this (log2 units) sends the workgroup to the
 // exact two-pass fallback; otherwise probabilities stay in (0, 2^32].
 constexpr float REF_GAP = 32.0f;
+
+// LDS layout (bytes)
+constexpr int LROW = 1040;                        // latent row stride (1024 + 16)
+constexpr int LAT_STAGE = TILE * LROW;            // 33280
+constexpr int NSTAGE = 4;
+constexpr int ROPE_SLOT = TILE * 128;             // 4096
+constexpr int NROPE = 3;
+constexpr int P_BUF = 128 * 64;                   // weights: 128 heads x 32 rows bf16
+constexpr int ROPE_OFF = NSTAGE * LAT_STAGE;      // 133120
+constexpr int P_OFF = ROPE_OFF + NROPE * ROPE_SLOT;   // 145408
+constexpr int LM_OFF = P_OFF + 2 * P_BUF;         // 161792: per-head (m, l), 1 KiB
+constexpr int FLAG_OFF = LM_OFF + 128 * 8;        // 162816
+constexpr int SMEM_BYTES = FLAG_OFF + 16;         // 162832 (of 163840)
+
+// Cache addressing modes (template argument).
+constexpr int CONTIG = 0;        // [B][capacity][576]
+constexpr int PAGED8 = 1;        // paged, block_size >= 8: 8-row groups share a block
+constexpr int PAGED_SMALL = 2;   // paged, block_size < 8
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -89,8 +121,17 @@ struct Params {
 __device__ __forceinline__ int rope_sw(int r) { return (r >> 1) & 7; }
 
 // First column of value block cb: blocks hold columns
-// colbase + {0..7} + 32 * {0..3}.
+// colbase + {0..7} + 32 * {0..3}. Blocks 4w..4w+3 cover columns
+// 128w..128w+127.
 __host__ __device__ constexpr int colbase(int cb) { return 8 * (cb % 4) + 128 * (cb / 4); }
+
+// Byte offset of weight slot (t, h) of head `head` in a weight buffer: a
+// head record is 64 B (logical rows 16t + 8h + 0..7 in slot 2t + h), slots
+// XOR-swizzled by (head >> 2) & 3 so that 16 consecutive heads hit distinct
+// bank groups.
+__device__ __forceinline__ int p_slot(int head, int t, int h) {
+  return head * 64 + 16 * ((2 * t + h) ^ ((head >> 2) & 3));
+}
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
 // [15:14], expcnt[6:4], lgkmcnt[11:8]; unconstrained fields at maximum).
@@ -105,9 +146,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // scalar load (it must not wait on the vector-memory counter, which also
 // tracks the LDS-DMA copies in flight).
 typedef __attribute__((address_space(4))) const int32_t const_i32;
-template <bool PAGED>
+template <int PM>
 __device__ __forceinline__ const uint16_t* row_ptr(const Params& p, int b, int u) {
-  if constexpr (!PAGED) {
+  if constexpr (PM == CONTIG) {
     return p.cache + b * p.seq_stride + static_cast<long long>(u) * DW;
   } else {
     const const_i32* tab = (const const_i32*)(p.table);
@@ -116,65 +157,137 @@ __device__ __forceinline__ const uint16_t* row_ptr(const Params& p, int b, int u
   }
 }
 
-// One LDS-DMA copy: every lane moves 16 bytes from its global address to LDS
-// at lds_base + 16 * lane. Written as inline asm so that the compiler does not
-// add its own (conservative, vmcnt(0)) waits in front of later LDS reads; the
-// kernel waits for these copies explicitly (wait_vmcnt + barrier). The copy
-// has no register result, and its address operands are read at issue.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+// LDS-DMA copies, written as inline asm so that the compiler adds none of its
+// own (conservative, vmcnt(0)) waits in front of later LDS reads; the kernel
+// waits for them explicitly (wait_vmcnt + barrier). A copy has no register
+// result and its address operands are read at issue. Every lane moves 16
+// bytes to LDS at lds + 16 * lane.
+//   copy_s: from row + voff (row wave-uniform, voff per lane)
+//   copy_v: from a per-lane 64-bit address
+__device__ __forceinline__ void copy_s(const uint16_t* row, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:0"
+               :: "s"(lds), "v"(voff), "s"(row));
+}
+__device__ __forceinline__ void copy_v(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_base), "v"(gptr) : "memory");
+               :: "s"(lds), "v"(gptr));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
 }
 
-// Issue this wave's 9 LDS-DMA copies of tile rows [r0, r0+32) into the stage
-// at LDS address `st`: the latents of rows 8w..8w+7 (1 KiB each, straight)
-// and the rotary parts of the same 8 rows (128 B each, one copy). Rows at or
-// past row_end are replaced by row_end-1 (a real row, later masked out of the
-// softmax), so no invalid address is ever read. w, r0, row_end are uniform.
-template <bool PAGED>
-__device__ __forceinline__ void issue_tile(const Params& p, uint32_t st, int b, int r0, int row_end,
-                                           int w, int lane) {
-  const uint16_t* rp[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) rp[k] = row_ptr<PAGED>(p, b, min(r0 + 8 * w + k, row_end - 1));
-#pragma unroll
-  for (int k = 0; k < 8; ++k) dma16(rp[k] + 8 * lane, st + (8 * w + k) * LROW);
-  // rotary block: lane -> row 8w + (lane >> 3), chunk (lane & 7) ^ rope_sw(row)
+// This wave's share of one tile copy: the latents of tile rows 8w..8w+7 (one
+// copy each) and the rotary parts of the same rows (one copy; lane -> row
+// 8w + (lane >> 3), chunk (lane & 7) ^ rope_sw(row)). Rows at or past
+// row_end are replaced by row_end - 1 (a real row, later masked out of the
+// softmax), so no invalid address is ever read. In CONTIG and PAGED8 modes
+// the rows of the group lie in one contiguous run (a group of 8 rows starting
+// at a multiple of 8 never crosses a block of >= 8 rows), so every copy is a
+// uniform base plus a per-lane offset.
+struct TileCopy {
+  const uint16_t* row[8];
+  const uint16_t* rope_base;   // CONTIG / PAGED8
+  uint32_t rope_voff;
+  const uint16_t* rope_ptr;    // PAGED_SMALL: per lane
+};
+
+template <int PM>
+__device__ __forceinline__ TileCopy plan_copy(const Params& p, int b, int r0, int row_end, int w, int lane) {
+  TileCopy c;
+  const int first = r0 + 8 * w;
+  const int last = row_end - 1;
   const int j = lane >> 3;
-  const uint16_t* mine = rp[0];
+  const int chunk = (lane & 7) ^ rope_sw(8 * w + j);
+  if constexpr (PM == PAGED_SMALL) {
 #pragma unroll
-  for (int k = 1; k < 8; ++k) mine = (j == k) ? rp[k] : mine;
-  const int c = (lane & 7) ^ rope_sw(8 * w + j);
-  dma16(mine + DC + 8 * c, st + LAT_BYTES + w * 1024);
+    for (int k = 0; k < 8; ++k) c.row[k] = row_ptr<PM>(p, b, min(first + k, last));
+    const uint16_t* mine = c.row[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mine = (j == k) ? c.row[k] : mine;
+    c.rope_ptr = mine + DC + 8 * chunk;
+    c.rope_base = nullptr;
+    c.rope_voff = 0;
+  } else {
+    const int g0 = min(first, last);
+    const uint16_t* base = row_ptr<PM>(p, b, g0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c.row[k] = base + (min(first + k, last) - g0) * DW;
+    c.rope_base = base;
+    c.rope_voff = (min(first + j, last) - g0) * ROW_BYTES + 2 * DC + 16 * chunk;
+    c.rope_ptr = nullptr;
+  }
+  return c;
+}
+
+// Copy k (0..8) of this wave's share: latents into the latent stage at LDS
+// address lat, the rotary block into the rotary slot at LDS address rope.
+template <int PM>
+__device__ __forceinline__ void copy_part(const TileCopy& c, int k, uint32_t lat, uint32_t rope, int w,
+                                          uint32_t lane_off) {
+  if (k < 8) {
+    copy_s(c.row[k], lane_off, lat + (8 * w + k) * LROW);
+  } else if constexpr (PM == PAGED_SMALL) {
+    copy_v(c.rope_ptr, rope + w * 1024);
+  } else {
+    copy_s(c.rope_base, c.rope_voff, rope + w * 1024);
+  }
 }
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Keeps a value in a register at this point of the instruction stream: the
+// computation producing it cannot sink below, nor its users rise above, the
+// neighbouring MFMA statements. Used to slot VALU work between MFMAs.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+template <typename T>
+__device__ __forceinline__ T pinned(T x) { asm volatile("" : "+v"(x)); return x; }
+
 // MFMA instructions issued from inline asm are invisible to the compiler's
 // hazard tracking. Where an operand is produced by the VALU (the zero
-// operand, the packed probabilities) the asm carries the VALU-write to
-// MFMA-read wait states itself; where the VALU reads an MFMA result next, the
-// wait states follow the MFMA inside the same asm statement, so no read can
-// be scheduled in between. All other operands come from memory loads, whose
+// operand) the asm carries the VALU-write to MFMA-read wait states itself;
+// where the VALU reads an MFMA result (the scores), explicit nops follow the
+// last MFMA of the chain. All other operands come from LDS reads, whose
 // completion the compiler's counter waits cover; a CPU test scans the
 // compiled ISA for every VALU write close before an MFMA that reads it.
 #define MLA_MFMA_PRE "s_nop 4\n\t"
-#define MLA_MFMA_POST "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
 
 // acc = 0 * 0 + 0: clears an accumulator block through the MFMA unit.
 __device__ __forceinline__ void mfma_zero(f32x16& acc, const bf16x8& zero8) {
   asm volatile(MLA_MFMA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero8));
 }
 
-template <int NW, bool PAGED>
+// Plain VALU maxima (inline asm: the inputs are finite or -inf, so none of
+// the NaN canonicalisation the compiler adds around fmaxf is needed).
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// max / sum over both half-waves (lanes l and l ^ 32), VALU only
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// NW = H / 32 head blocks. Waves w >= NW (H < 128) compute the scores of head
+// block w % NW a second time and write identical weights, which keeps every
+// wave on one branch-free path.
+template <int NW, int PM>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma_kernel(Params p) {
-  __shared__ __align__(1024) char smem[NSTAGE * STAGE];
-  __shared__ int wg_flag;
+  __shared__ __align__(1024) char smem[SMEM_BYTES];
   const uint32_t smem_lds = lds_addr(smem);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -183,228 +296,329 @@ void attn_mfma_kernel(Params p) {
   const int l32 = lane & 31;
   const int s_idx = blockIdx.x % p.splits;
   const int b = blockIdx.x / p.splits;
+  const int hq = w % NW;              // this wave's score head block
+  const int qhead = 32 * hq + l32;    // this lane's score head
 
   const int L = p.seq_lens[b];
   const int row_begin = s_idx * p.chunk;
   const int row_end = min(row_begin + p.chunk, L);
-  const bool active = w < NW;
-  const int head = 32 * w + l32;
 
   if (row_begin >= row_end) {
     // Nothing to attend in this chunk. With splits > 1 the combine kernel
-    // skips it; with a single split the sequence is empty.
-    if (p.splits == 1 && active) {
-      float* o = p.o_lat + (static_cast<long long>(b) * p.H + head) * DC;
+    // skips it; with a single split the sequence is empty: zeros, lse -inf.
+    if (p.splits == 1 && w < NW) {
+      float* o = p.o_lat + (static_cast<long long>(b) * p.H + qhead) * DC;
       for (int c = h * 256; c < h * 256 + 256; c += 4)
         *reinterpret_cast<f32x4*>(o + c) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (p.lse && h == 0) p.lse[b * p.H + head] = -INFINITY;
+      if (p.lse && h == 0) p.lse[b * p.H + qhead] = -INFINITY;
     }
     return;
   }
   const int ntiles = (row_end - row_begin + TILE - 1) / TILE;
+  const uint32_t lane_off = 16 * lane;
 
   // Query of this lane's head in MFMA B-operand order: step s, half h holds
   // columns 16s + 8h .. 16s + 8h + 7.
-  bf16x8 qreg[36];
-  if (active) {
-    const uint16_t* qp = p.q + (static_cast<long long>(b) * p.H + head) * DW + 8 * h;
+  bf16x8 qreg[QK_STEPS];
+  {
+    const uint16_t* qp = p.q + (static_cast<long long>(b) * p.H + qhead) * DW + 8 * h;
 #pragma unroll
-    for (int s = 0; s < 36; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    for (int s = 0; s < QK_STEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
+  // O^T accumulators: block (c, hb) holds columns of value block 4w + c
+  // against heads 32hb..32hb+31.
   const bf16x8 zero8 = {};
-  f32x16 oacc[16];
+  f32x16 oacc[4 * NW];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) mfma_zero(oacc[i], zero8);
-  float m_ref = -INFINITY;   // reference maximum, log2 units
-  float l_run = 0.f;         // this lane's partial sum (its 16 of each 32 rows)
+  for (int i = 0; i < 4 * NW; ++i) mfma_zero(oacc[i], zero8);
+  float m_ref = -INFINITY;   // reference maximum, log2 units (score heads)
+  float l_run = 0.f;         // this lane's partial weight sum
 
-  // Per-lane LDS bases inside a stage; every other part of an operand address
-  // is a compile-time immediate of the unrolled loops below.
+  // Per-lane LDS bases; every other part of an operand address is a
+  // compile-time immediate of the unrolled loops below.
   //  score operand: row l32, latent chunk 2s + h at 16 * (2s + h)
   const int qk_base = l32 * LROW + 16 * h;
   //  rotary part of row l32: chunk c' at 16 * (c' ^ rope_sw(l32))
-  const int rp_base = LAT_BYTES + l32 * 128;
+  const int rp_base = l32 * 128;
   const int rp_sw = rope_sw(l32);
   //  value operand, transposed read: in its 16-lane group a lane supplies row
   //  16t + 8k + 4*(g16>>1) + tr_e, 8 bytes at column colbase(cb) + 32*tr_q + 4*(g16&1)
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int tr_base = (4 * (g16 >> 1) + (i16 >> 2)) * LROW + 64 * (i16 & 3) + 8 * (g16 & 1);
+  const int tr_base = (4 * (g16 >> 1) + (i16 >> 2)) * LROW + 64 * (i16 & 3) + 8 * (g16 & 1) + 2 * colbase(4 * w);
+  //  weight operand of head 32hb + l32, slot (t, h): p_slot minus 2048 hb
+  const int pr_base0 = p_slot(l32, 0, h), pr_base1 = p_slot(l32, 1, h);
 
-  // mode 0: fast pass (first-tile reference); mode 1: scores only, exact
-  // maximum (fallback); mode 2: full pass against that maximum (fallback).
-  int mode = 0;
-  for (;;) {
-    // Prologue: tiles 0..NSTAGE-2 in flight. Then wait for everything issued
-    // so far (the query and these copies) so that no vector-memory wait stays
-    // pending inside the loop: the loop's waits are the explicit ones below.
+  auto lat_off = [&](int t) { return (t % NSTAGE) * LAT_STAGE; };
+  auto rope_off = [&](int t) { return ROPE_OFF + (t % NROPE) * ROPE_SLOT; };
+  auto p_off = [&](int t) { return P_OFF + (t & 1) * P_BUF; };
+  auto tile_r0 = [&](int t) { return row_begin + t * TILE; };
+  auto tile_nv = [&](int t) { return min(TILE, row_end - tile_r0(t)); };
+  auto copy_tile = [&](int t) {
+    const TileCopy c = plan_copy<PM>(p, b, tile_r0(t), row_end, w, lane);
 #pragma unroll
-    for (int j = 0; j < NSTAGE - 1; ++j)
-      if (j < ntiles) issue_tile<PAGED>(p, smem_lds + j * STAGE, b, row_begin + j * TILE, row_end, w, lane);
-    wait_vmcnt<0>();
-    bool grew = false;
-    float m_seen = -INFINITY;
+    for (int k = 0; k < DMA_PER_WAVE; ++k)
+      copy_part<PM>(c, k, smem_lds + lat_off(t), smem_lds + rope_off(t), w, lane_off);
+  };
 
-    for (int it = 0; it < ntiles; ++it) {
-      // Tile `it` was issued NSTAGE-1 iterations ago; later tiles may still fly.
-      const int later = min(ntiles - 1 - it, NSTAGE - 2);
-      if (later >= 2) wait_vmcnt<2 * DMA_PER_WAVE>();
-      else if (later == 1) wait_vmcnt<DMA_PER_WAVE>();
-      else wait_vmcnt<0>();
-      block_barrier();
-      if (it + NSTAGE - 1 < ntiles)
-        issue_tile<PAGED>(p, smem_lds + ((it + NSTAGE - 1) % NSTAGE) * STAGE, b,
-                          row_begin + (it + NSTAGE - 1) * TILE, row_end, w, lane);
-      if (!active) continue;
-
-      const char* st = smem + (it % NSTAGE) * STAGE;
-      const int nv = min(TILE, row_end - (row_begin + it * TILE));
-
-      // ---- scores: S^T[row][head] over all 576 columns ----
-      // Two accumulation chains (even / odd steps); operand reads run two
-      // steps ahead of the MFMA that consumes them.
-      auto qk_operand = [&](int s) -> bf16x8 {
-        const char* ap = (s < 32) ? st + qk_base + 32 * s
-                                  : st + rp_base + 16 * ((2 * (s - 32) + h) ^ rp_sw);
-        return *reinterpret_cast<const bf16x8*>(ap);
-      };
-      f32x16 sacc0, sacc1;
-      bf16x8 a0 = qk_operand(0), a1 = qk_operand(1);
+  // S^T[row][head] of one tile over all 576 columns, one accumulation chain;
+  // between(s) runs after the MFMA of step s.
+  auto qk = [&](int t, f32x16& acc, auto&& between) {
+    const char* lat = smem + lat_off(t);
+    const char* rope = smem + rope_off(t);
+    auto operand = [&](int s) -> bf16x8 {
+      const char* ap = (s < 32) ? lat + qk_base + 32 * s
+                                : rope + rp_base + 16 * ((2 * (s - 32) + h) ^ rp_sw);
+      return *reinterpret_cast<const bf16x8*>(ap);
+    };
+    bf16x8 a[QK_DIST];
 #pragma unroll
-      for (int s = 0; s < 36; ++s) {
-        const bf16x8 a2 = (s + 2 < 36) ? qk_operand(s + 2) : a0;
-        if (s == 0) {
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc0) : "v"(a0), "v"(qreg[s]));
-        } else if (s == 1) {
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc1) : "v"(a0), "v"(qreg[s]));
-        } else if (s < 35) {
-          if (s & 1)
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc1) : "v"(a0), "v"(qreg[s]));
-          else
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc0) : "v"(a0), "v"(qreg[s]));
-        } else {
-          // last step: the VALU reads both chains next
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0" MLA_MFMA_POST
-                       : "+v"(sacc1), "+v"(sacc0) : "v"(a0), "v"(qreg[s]));
-        }
-        a0 = a1;
-        a1 = a2;
+    for (int i = 0; i < QK_DIST; ++i) a[i] = operand(i);
+#pragma unroll
+    for (int s = 0; s < QK_STEPS; ++s) {
+      const bf16x8 cur = a[s % QK_DIST];
+      if (s + QK_DIST < QK_STEPS) a[s % QK_DIST] = operand(s + QK_DIST);
+      if (s == 0)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(cur), "v"(qreg[s]));
+      else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(cur), "v"(qreg[s]));
+      between(s);
+    }
+    // the VALU reads the scores next
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc));
+  };
+
+  // O^T[cols of this wave][all heads] += V^T P for tile t, weights from the
+  // weight buffer of tile t. Steps run (k-step, c, hb) in that order;
+  // between(step) runs after each MFMA.
+  constexpr int PV_STEPS = 8 * NW;
+  auto pv = [&](int t, auto&& between) {
+    const char* lat = smem + lat_off(t);
+    const char* pw = smem + p_off(t);
+    auto v_operand = [&](int vi) -> bf16x8 {   // vi = 4 * kstep + c
+      const char* a = lat + tr_base + (16 * LROW) * (vi >> 2) + 16 * (vi & 3);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * LROW));
+      return __builtin_bit_cast(bf16x8, (s16x8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+    };
+    auto p_operand = [&](int hb, int ks) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(pw + (ks ? pr_base1 : pr_base0) + 2048 * hb);
+    };
+    bf16x8 P[NW];
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) P[hb] = p_operand(hb, 0);
+    bf16x8 V[PV_DIST];
+#pragma unroll
+    for (int i = 0; i < PV_DIST; ++i) V[i] = v_operand(i);
+    int step = 0;
+#pragma unroll
+    for (int vi = 0; vi < 8; ++vi) {
+      const bf16x8 cur = V[vi % PV_DIST];
+      if (vi + PV_DIST < 8) V[vi % PV_DIST] = v_operand(vi + PV_DIST);
+      const int c = vi & 3;
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb) {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+a"(oacc[4 * c + hb]) : "v"(cur), "v"(P[hb]));
+        if (vi == 3) P[hb] = p_operand(hb, 1);   // last use of the first k-step's weights
+        between(step++);
       }
-      f32x16 sacc = sacc0 + sacc1;
+    }
+  };
 
-      // ---- softmax weights (base 2) against the reference maximum ----
-      // Scores are scaled once (x = s * scale * log2 e); the maximum and the
-      // exponents use the same rounded x, so a row at the reference gets
-      // weight exactly 1.
-      sacc *= p.sl2;
-      if (nv < TILE) {
+  // ---- softmax of one tile, as a sequence of small steps ----
+  // x: the tile's raw scores (lane: head qhead, register r <-> row
+  // 8*(r>>2) + 4h + (r&3)); nv: valid rows; set_ref: this tile sets the
+  // reference (fast pass, first tile). Writes the tile's bf16 weights to its
+  // weight buffer (slot (t, h) holds registers 8t..8t+7) and adds them into
+  // l_run. In log2 units a score is x = s * sl2; the tile maximum is taken on
+  // raw scores (scaling by sl2 > 0 preserves order), m = round(max * sl2),
+  // and each weight is exp2(fma(s, sl2, -m_ref)). The normaliser sums the
+  // bf16-rounded weights, i.e. exactly the weights the value MFMAs apply (so
+  // a single row reproduces its latent exactly). Each step is a few
+  // independent VALU instructions, sized to sit under one MFMA.
+  struct Soft {
+    f32x16 x;
+    float mx[7];
+    float psum;
+    bf16x8 pb[2];
+  };
+  constexpr int SM_STEPS = 29;
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  // Every step pins the values it reads on entry and those it writes on
+  // exit (pin/pinned: empty volatile asm), so its instructions can move
+  // neither above nor below the MFMAs around it.
+  auto soft_step = [&](Soft& S, int k, int nv, bool set_ref, bool& grew, int pbuf) {
+    if (k == 0) {
+#pragma unroll
+      for (int r = 0; r < 12; ++r) S.x[r] = pinned(S.x[r]);
+      if (nv < TILE) {                  // mask rows past the end (last tile only)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + 4 * h + (r & 3) >= nv) sacc[r] = -INFINITY;
+          if (8 * (r >> 2) + 4 * h + (r & 3) >= nv) S.x[r] = -INFINITY;
       }
-      float tmax = sacc[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      if (mode == 1) {
-        m_seen = fmaxf(m_seen, tmax);
-        continue;
+      for (int i = 0; i < 4; ++i) S.mx[i] = pinned(max3(S.x[3 * i], S.x[3 * i + 1], S.x[3 * i + 2]));
+    } else if (k == 1) {
+#pragma unroll
+      for (int r = 12; r < 16; ++r) S.x[r] = pinned(S.x[r]);
+      S.mx[4] = max3(S.x[12], S.x[13], S.x[14]);
+      S.mx[5] = pinned(max3(S.mx[0], S.mx[1], S.x[15]));
+      S.mx[6] = pinned(max3(S.mx[2], S.mx[3], S.mx[4]));
+    } else if (k == 2) {
+      S.mx[0] = pinned(max_halves(max2(S.mx[5], S.mx[6])));
+    } else if (k == 3) {
+      const float tmax = S.mx[0] * p.sl2;
+      if (set_ref) m_ref = tmax;
+      else grew = grew || (tmax > m_ref + REF_GAP);
+      pin(m_ref);
+      S.psum = 0.f;
+    } else if (k < 20) {                // 4..19: one weight per step
+      const int r = k - 4;
+      S.x[r] = pinned(__builtin_amdgcn_exp2f(__builtin_fmaf(pinned(S.x[r]), p.sl2, -m_ref)));
+    } else if (k < 28) {                // 20..27: pack a pair to bf16, add it to the sum
+      const int i = k - 20, t = i >> 2, e = i & 3;
+      const float x0 = pinned(S.x[8 * t + 2 * e]), x1 = pinned(S.x[8 * t + 2 * e + 1]);
+      const bf16x2 v2 = __builtin_convertvector((f32x2{x0, x1}), bf16x2);
+      S.pb[t][2 * e] = v2[0];
+      S.pb[t][2 * e + 1] = v2[1];
+      S.psum = pinned(__builtin_amdgcn_fdot2_f32_bf16(v2, ones2, S.psum, false));
+      if (e == 3) {
+        pin(S.pb[t]);
+        char* dst = smem + pbuf + 2048 * hq + (t ? pr_base1 : pr_base0);
+        *reinterpret_cast<bf16x8*>(dst) = S.pb[t];
       }
-      if (mode == 0) {
-        if (it == 0) m_ref = tmax;
-        else grew = grew || (tmax > m_ref + REF_GAP);
-      }
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - m_ref);
-        psum += sacc[r];
-      }
-      l_run += psum;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          bf16x2 v2 = __builtin_convertvector((f32x2{sacc[8 * t + 2 * k], sacc[8 * t + 2 * k + 1]}), bf16x2);
-          pb[t][2 * k] = v2[0];
-          pb[t][2 * k + 1] = v2[1];
-        }
-      // P was just written by the VALU and is read by MFMAs next (VALU-write
-      // to MFMA-read wait states, tied to the operands).
-      asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]));
-
-      // ---- O^T[col][head] += V^T P ----
-      // Steps run t-major (all 16 column blocks for rows 0-15, then rows
-      // 16-31) so that the two MFMAs into one accumulator are 16 apart; the
-      // transposed operand reads run two steps ahead.
-      auto pv_operand = [&](int cb, int t) -> bf16x8 {
-        const char* a = st + tr_base + (16 * LROW) * t + 2 * colbase(cb);
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * LROW));
-        return __builtin_bit_cast(bf16x8, (s16x8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-      };
-      bf16x8 v0 = pv_operand(0, 0), v1 = pv_operand(1, 0);
-#pragma unroll
-      for (int step = 0; step < 32; ++step) {
-        const int t = step >> 4, cb = step & 15;
-        const bf16x8 v2 = (step + 2 < 32) ? pv_operand((step + 2) & 15, (step + 2) >> 4) : v0;
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(oacc[cb]) : "v"(v0), "v"(pb[t]));
-        v0 = v1;
-        v1 = v2;
-      }
-    }
-
-    if (mode == 2) break;
-    if (mode == 1) {
-      // exact maximum known: redo the chunk against it
-      m_ref = m_seen;
-      l_run = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mfma_zero(oacc[i], zero8);
-      mode = 2;
-      __syncthreads();
-      continue;
-    }
-    // mode 0 done: did any head in the workgroup outgrow its reference?
-    if (tid == 0) wg_flag = 0;
-    __syncthreads();
-    if (active && __builtin_amdgcn_ballot_w64(grew) != 0 && lane == 0) wg_flag = 1;
-    __syncthreads();
-    if (wg_flag == 0) break;
-    mode = 1;
-    __syncthreads();
-  }
-
-  if (!active) return;
-  // The accumulators are read next; cover the last MFMAs' latency.
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = (p.splits == 1) ? 1.f / l_tot : 1.f;
-  float* o = (p.splits == 1)
-                 ? p.o_lat + (static_cast<long long>(b) * p.H + head) * DC
-                 : p.part_o + ((static_cast<long long>(b) * p.splits + s_idx) * p.H + head) * DC;
-  // D[i][head] of block cb holds column colbase(cb) + 32*((i&15)>>2) + 4*(i>>4) + (i&3);
-  // register 4g + m of this lane is i = 8g + 4h + m.
-#pragma unroll
-  for (int cb = 0; cb < 16; ++cb) {
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[cb][r]));
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int col = colbase(cb) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
-      *reinterpret_cast<f32x4*>(o + col) =
-          f32x4{x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv};
-    }
-  }
-  if (h == 0) {
-    if (p.splits == 1) {
-      if (p.lse) p.lse[b * p.H + head] = (m_ref + log2f(l_tot)) * 0.69314718055994531f;
     } else {
-      const long long pidx = (static_cast<long long>(b) * p.splits + s_idx) * p.H + head;
+      l_run += S.psum;
+    }
+  };
+
+  // ---- fast pass (reference from the first tile) or, with fixed_ref, the
+  // exact second pass against known maxima ----
+  auto full_pass = [&](bool fixed_ref) -> bool {
+#pragma unroll
+    for (int j = 0; j < NSTAGE - 1; ++j)
+      if (j < ntiles) copy_tile(j);
+    // Wait for everything issued so far (the query and these copies) so that
+    // no vector-memory wait stays pending inside the loop.
+    wait_vmcnt<0>();
+    block_barrier();
+    bool grew = false;
+    {
+      Soft S;
+      qk(0, S.x, [](int) {});
+#pragma unroll
+      for (int k = 0; k < SM_STEPS; ++k) soft_step(S, k, tile_nv(0), !fixed_ref, grew, p_off(0));
+    }
+    // Iteration t: tile t+1 has landed (only the copies of tile t+2 may
+    // still fly), every wave has written the weights of tile t and is past
+    // tile t-1, whose stages tile t+3 reuses.
+    int t = 0;
+    for (; t + 1 < ntiles; ++t) {
+      if (t + 2 < ntiles) wait_vmcnt<DMA_PER_WAVE>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      const bool copy_next = t + 3 < ntiles;
+      const TileCopy c = plan_copy<PM>(p, b, tile_r0(copy_next ? t + 3 : t), row_end, w, lane);
+      const uint32_t lat3 = smem_lds + lat_off(t + 3), rope3 = smem_lds + rope_off(t + 3);
+      Soft N;
+      qk(t + 1, N.x, [&](int s) {
+        if (s % 4 == 1 && s / 4 < DMA_PER_WAVE && copy_next) copy_part<PM>(c, s / 4, lat3, rope3, w, lane_off);
+      });
+      const int nv = tile_nv(t + 1), pb_next = p_off(t + 1);
+      pv(t, [&](int step) {
+        if (step < SM_STEPS) soft_step(N, step, nv, false, grew, pb_next);
+      });
+#pragma unroll
+      for (int k = PV_STEPS; k < SM_STEPS; ++k) soft_step(N, k, nv, false, grew, pb_next);
+    }
+    // last tile: its weights are complete once every wave is here
+    block_barrier();
+    pv(t, [](int) {});
+    return grew;
+  };
+
+  // ---- fallback scores-only pass: exact per-head maximum over the chunk ----
+  // Copies run two tiles ahead (iteration t refills the stages of tile t-2
+  // and the rotary slot of tile t-1, both finished before its barrier).
+  auto max_pass = [&]() -> float {
+    float m_seen = -INFINITY;
+    copy_tile(0);
+    if (1 < ntiles) copy_tile(1);
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 1 < ntiles) wait_vmcnt<DMA_PER_WAVE>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      if (t + 2 < ntiles) copy_tile(t + 2);
+      f32x16 x;
+      qk(t, x, [](int) {});
+      const int nv = tile_nv(t);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * h + (r & 3) >= nv) x[r] = -INFINITY;
+      float tmax = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = max2(tmax, x[r]);
+      m_seen = max2(m_seen, max_halves(tmax) * p.sl2);
+    }
+    return m_seen;
+  };
+
+  int* wg_flag = reinterpret_cast<int*>(smem + FLAG_OFF);
+  bool grew = full_pass(false);
+  // did any head in the workgroup outgrow its reference?
+  if (tid == 0) *wg_flag = 0;
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(grew) != 0 && lane == 0) *wg_flag = 1;
+  __syncthreads();
+  if (*wg_flag != 0) {
+    __syncthreads();
+    const float m_exact = max_pass();
+    __syncthreads();
+    m_ref = m_exact;
+    l_run = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4 * NW; ++i) mfma_zero(oacc[i], zero8);
+    full_pass(true);
+  }
+
+  // Per-head (m, l) through LDS: the value split needs every head's l.
+  float* lm = reinterpret_cast<float*>(smem + LM_OFF);
+  const float l_tot = sum_halves(l_run);
+  if (w < NW && h == 0) {
+    lm[2 * qhead] = m_ref;
+    lm[2 * qhead + 1] = l_tot;
+    if (p.splits == 1) {
+      if (p.lse) p.lse[b * p.H + qhead] = (m_ref + log2f(l_tot)) * 0.69314718055994531f;
+    } else {
+      const long long pidx = (static_cast<long long>(b) * p.splits + s_idx) * p.H + qhead;
       p.part_ml[pidx * 2] = m_ref;
       p.part_ml[pidx * 2 + 1] = l_tot;
+    }
+  }
+  __syncthreads();
+  // The accumulators are read next; cover the last MFMAs' latency.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // D[i][head] of block (c, hb) holds column colbase(4w + c) + 32*((i&15)>>2)
+  // + 4*(i>>4) + (i&3); register 4g + m of this lane is i = 8g + 4h + m.
+#pragma unroll
+  for (int hb = 0; hb < NW; ++hb) {
+    const int head = 32 * hb + l32;
+    const float inv = (p.splits == 1) ? 1.f / lm[2 * head + 1] : 1.f;
+    float* o = (p.splits == 1)
+                   ? p.o_lat + (static_cast<long long>(b) * p.H + head) * DC
+                   : p.part_o + ((static_cast<long long>(b) * p.splits + s_idx) * p.H + head) * DC;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[4 * c + hb][r]));
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = colbase(4 * w + c) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
+        *reinterpret_cast<f32x4*>(o + col) =
+            f32x4{x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv};
+      }
     }
   }
 }
@@ -429,10 +643,11 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
   p.part_o = a.part_o;
   p.part_ml = a.part_ml;
   const dim3 grid(a.B * a.splits);
-  const bool paged = a.block_table != nullptr;
-#define MLA_ATTN_LAUNCH(NW)                                                          \
-  if (paged) attn_mfma_kernel<NW, true><<<grid, NTHREADS, 0, stream>>>(p);           \
-  else attn_mfma_kernel<NW, false><<<grid, NTHREADS, 0, stream>>>(p);
+  const int pm = !a.block_table ? CONTIG : (a.block_size >= 8 ? PAGED8 : PAGED_SMALL);
+#define MLA_ATTN_LAUNCH(NW)                                                               \
+  if (pm == CONTIG) attn_mfma_kernel<NW, CONTIG><<<grid, NTHREADS, 0, stream>>>(p);       \
+  else if (pm == PAGED8) attn_mfma_kernel<NW, PAGED8><<<grid, NTHREADS, 0, stream>>>(p);  \
+  else attn_mfma_kernel<NW, PAGED_SMALL><<<grid, NTHREADS, 0, stream>>>(p);
   switch (a.H / 32) {
     case 1: MLA_ATTN_LAUNCH(1) break;
     case 2: MLA_ATTN_LAUNCH(2) break;
