@@ -146,13 +146,26 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
     den += exp2f(a.part_ml[pi * 2] - M) * a.part_ml[pi * 2 + 1];
   }
   const float inv = (den > 0.f) ? 1.f / den : 0.f;
-  for (int c = threadIdx.x; c < a.d_c; c += blockDim.x) {
-    float x = 0.f;
-    for (int s = 0; s < nv; ++s) {
-      const long long pi = base + static_cast<long long>(s) * a.H;
-      x += exp2f(a.part_ml[pi * 2] - M) * a.part_o[pi * a.d_c + c];
+  if ((a.d_c & 3) == 0) {
+    // four columns per thread, streamed once (partials are not reused)
+    for (int c = 4 * threadIdx.x; c < a.d_c; c += 4 * blockDim.x) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < nv; ++s) {
+        const long long pi = base + static_cast<long long>(s) * a.H;
+        const float ws = exp2f(a.part_ml[pi * 2] - M);
+        x += ws * __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.part_o + pi * a.d_c + c));
+      }
+      *reinterpret_cast<f32x4*>(o + c) = x * inv;
     }
-    o[c] = x * inv;
+  } else {
+    for (int c = threadIdx.x; c < a.d_c; c += blockDim.x) {
+      float x = 0.f;
+      for (int s = 0; s < nv; ++s) {
+        const long long pi = base + static_cast<long long>(s) * a.H;
+        x += exp2f(a.part_ml[pi * 2] - M) * a.part_o[pi * a.d_c + c];
+      }
+      o[c] = x * inv;
+    }
   }
   if (a.lse && threadIdx.x == 0)
     a.lse[b * a.H + head] = (den > 0.f) ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;

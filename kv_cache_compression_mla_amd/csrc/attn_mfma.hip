@@ -499,9 +499,11 @@ void attn_mfma_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
       if (j < ntiles) copy_tile(j);
-    // Wait for everything issued so far (the query and these copies) so that
-    // no vector-memory wait stays pending inside the loop.
-    wait_vmcnt<0>();
+    // Wait for the query (loaded first) and tile 0; tiles 1 and 2 may still
+    // fly. The loop's waits count only these copies: nothing else in flight.
+    if (ntiles >= 3) wait_vmcnt<2 * DMA_PER_WAVE>();
+    else if (ntiles == 2) wait_vmcnt<DMA_PER_WAVE>();
+    else wait_vmcnt<0>();
     block_barrier();
     bool grew = false;
     {
