@@ -18,7 +18,7 @@ The absorbed companion (decode_step_absorbed) regroups the same arithmetic
 the way the decode form does; it supplies references for the intermediate
 tensors (absorbed query, latent-space output).
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
   * ctx counts rows already cached; the new token is stored at position ctx
     and attention covers ctx + 1 rows, itself included ([CASS] "End-to-end
     flow": append, then attend over all history).
