@@ -33,6 +33,9 @@ struct GemmP {
   const uint16_t* W; long long ldw, sWg;
   int M, N, K, ksplit;    // ksplit = k per split (multiple of GBK)
   float* P;
+  void* out;              // direct store (streaming kernel, one split) or NULL
+  long long ldo, sOg;
+  int out_bf16;
 };
 
 template <int MT, bool A_F32, bool W_KN>
@@ -170,6 +173,226 @@ __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming skinny GEMM for [out][in] weights ("NT"), K a multiple of 64.
+//   P[split][g][m][n] = sum over the split's k range of A_g[m][k] * W_g[n][k]
+// A workgroup owns 64 weight rows (output columns) and all rows of A in its
+// m block (32*MT), over one k range. Weight and activation tiles of 64 k go
+// HBM -> LDS by LDS-DMA (global_load_lds_dwordx4, 1 KiB per copy) through a
+// ring of NS stages, so several stages of weights are in flight per
+// workgroup and no register staging is needed. In LDS a 64-k row keeps its
+// 16-byte chunks XOR-swizzled (chunk c of row r at slot c ^ ((r >> 1) & 7);
+// fp32 activation rows: 16 chunks, slot c ^ (r & 15)); the copy picks the
+// source chunk of each destination slot, and the MFMA operand reads
+// (ds_read_b128, 16 lanes = 16 rows of one chunk) are bank-conflict free.
+// A workgroup owns NT = 64 or 128 weight rows. Waves: w % (NT/32) picks a
+// 32-column block; with NT = 64 the other bit picks a 32-k half of each
+// stage, and the two k halves are summed through LDS at the end.
+// ---------------------------------------------------------------------------
+// weight rows per workgroup: 128 for wide outputs (halves the activation
+// re-reads), 64 otherwise (more workgroups on narrow outputs)
+__host__ __device__ constexpr int stream_nt(int N) { return N >= 4096 ? 128 : 64; }
+constexpr int SKT = 64;      // k per stage
+
+template <int N>
+__device__ __forceinline__ void s_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One LDS-DMA copy: each lane moves 16 bytes from its address to LDS at
+// lds + 16 * lane. Inline asm so that the compiler adds no vmcnt(0) waits in
+// front of later LDS reads; the kernel waits for its copies explicitly.
+__device__ __forceinline__ void dma_copy(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(gptr));
+}
+
+// Wait until at most later * PW copies are in flight (later <= MAXL).
+template <int PW, int MAXL>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (MAXL > 0) {
+    if (later == MAXL) {
+      s_wait_vmcnt<MAXL * PW>();
+      return;
+    }
+    wait_later<PW, MAXL - 1>(later);
+  } else {
+    s_wait_vmcnt<0>();
+  }
+}
+
+template <int NT, int MT, bool A_F32>
+struct StreamCfg {
+  static constexpr int NB = NT / 32;                           // 32-column blocks
+  static constexpr int KH = 4 / NB;                            // k halves per stage
+  static constexpr int A_ROW = A_F32 ? 256 : 128;              // bytes of one 64-k activation row
+  static constexpr int W_BYTES = NT * 128;
+  static constexpr int A_BYTES = 32 * MT * A_ROW;
+  static constexpr int STAGE = W_BYTES + A_BYTES;
+  // one workgroup per CU with up to 144 KiB of ring, so that ~64 KiB of
+  // weights are in flight per CU; never fewer than 3 stages
+  static constexpr int NS0 = 144 * 1024 / STAGE;
+  static constexpr int NS = NS0 > 9 ? 9 : (NS0 < 3 ? 3 : NS0);
+  static constexpr int COPIES = STAGE / 1024;                  // per stage
+  static constexpr int PER_WAVE = COPIES / 4;
+  static_assert(COPIES % 4 == 0, "copies split evenly over four waves");
+  static_assert(NS >= 3, "at least three stages");
+  static_assert((NS - 1) * PER_WAVE < 64, "copies in flight fit the vmcnt counter");
+};
+
+template <int NT, int MT, bool A_F32>
+__global__ __launch_bounds__(GTH) void gemm_stream_kernel(GemmP p) {
+  using C = StreamCfg<NT, MT, A_F32>;
+  __shared__ __align__(1024) char smem[C::NS * C::STAGE];
+  const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)smem));
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5, l32 = lane & 31;
+  const int nh = w % C::NB, kh = w / C::NB;
+  const int n0 = blockIdx.x * NT;
+  const int g = blockIdx.y;
+  const int mblocks = (p.M + 32 * MT - 1) / (32 * MT);
+  const int split = blockIdx.z / mblocks;
+  const int m0 = (blockIdx.z % mblocks) * 32 * MT;
+  const int k_begin = split * p.ksplit;
+  const int k_end = min(p.K, k_begin + p.ksplit);
+  const int nsteps = k_end > k_begin ? (k_end - k_begin) / SKT : 0;
+  const uint16_t* W = p.W + g * p.sWg;
+
+  // copy i of a stage (0..COPIES-1) for this lane: source address and LDS offset
+  auto issue_stage = [&](int t) {
+    const int kb = k_begin + t * SKT;
+    const uint32_t st = sbase + (t % C::NS) * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < C::PER_WAVE; ++j) {
+      const int i = w * C::PER_WAVE + j;
+      if (i < NT / 8) {                              // weight rows 8i..8i+7
+        const int r = 8 * i + (lane >> 3), slot = lane & 7;
+        const int c = slot ^ ((r >> 1) & 7);
+        const int n = min(n0 + r, p.N - 1);
+        dma_copy(W + static_cast<long long>(n) * p.ldw + kb + 8 * c, st + 1024 * i);
+      } else if constexpr (!A_F32) {                  // activation rows, bf16
+        const int a = i - NT / 8;
+        const int r = 8 * a + (lane >> 3), slot = lane & 7;
+        const int c = slot ^ ((r >> 1) & 7);
+        const int m = min(m0 + r, p.M - 1);
+        const uint16_t* A = static_cast<const uint16_t*>(p.A) + g * p.sAg;
+        dma_copy(A + static_cast<long long>(m) * p.lda + kb + 8 * c, st + C::W_BYTES + 1024 * a);
+      } else {                                        // activation rows, fp32
+        const int a = i - NT / 8;
+        const int r = 4 * a + (lane >> 4), slot = lane & 15;
+        const int c = slot ^ (r & 15);
+        const int m = min(m0 + r, p.M - 1);
+        const float* A = static_cast<const float*>(p.A) + g * p.sAg;
+        dma_copy(A + static_cast<long long>(m) * p.lda + kb + 4 * c, st + C::W_BYTES + 1024 * a);
+      }
+    }
+  };
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x16{};
+
+  if (nsteps > 0) {
+#pragma unroll
+    for (int j = 0; j < C::NS - 1; ++j)
+      if (j < nsteps) issue_stage(j);
+    for (int t = 0; t < nsteps; ++t) {
+      // stage t landed: only the copies of stages t+1 .. t+NS-2 may still fly
+      const int later = min(nsteps - 1 - t, C::NS - 2);
+      wait_later<C::PER_WAVE, C::NS - 2>(later);
+      // plain barrier: __syncthreads would also wait for the copies in flight
+      asm volatile("s_barrier" ::: "memory");
+      // every wave is past stage t-1: its slot takes stage t+NS-1
+      if (t + C::NS - 1 < nsteps) issue_stage(t + C::NS - 1);
+      const char* st = smem + (t % C::NS) * C::STAGE;
+#pragma unroll
+      for (int j2 = 0; j2 < 4 / C::KH; ++j2) {
+        const int j = (4 / C::KH) * kh + j2;          // k16 step of this wave
+        const int rw = 32 * nh + l32, cw = 2 * j + h;
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(st + 16 * (rw * 8 + (cw ^ ((rw >> 1) & 7))));
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const int ra = 32 * i + l32;
+          bf16x8 av;
+          if constexpr (!A_F32) {
+            av = *reinterpret_cast<const bf16x8*>(st + C::W_BYTES + 16 * (ra * 8 + (cw ^ ((ra >> 1) & 7))));
+          } else {
+            const char* arow = st + C::W_BYTES + ra * 256;
+            const int c0 = 2 * cw, c1 = 2 * cw + 1;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(arow + 16 * (c0 ^ (ra & 15)));
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(arow + 16 * (c1 ^ (ra & 15)));
+            av = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                                                  pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])});
+          }
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), av, acc[i], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if constexpr (C::KH == 2) {
+    // sum the two k halves: waves 2,3 hand their accumulators to waves 0,1
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((nh * MT + i) * 16 + r) * 64 + lane] = acc[i][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] += red[((nh * MT + i) * 16 + r) * 64 + lane];
+  }
+  // D[n][m]: lane holds m = 32i + l32, n = 32nh + 8(r/4) + 4h + r%4.
+  if (p.out) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + 32 * i + l32;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 32 * nh + 8 * q + 4 * h;
+        const long long o = g * p.sOg + static_cast<long long>(m) * p.ldo + n;
+        if (p.out_bf16) {
+          uint16_t* dst = static_cast<uint16_t*>(p.out) + o;
+          if (n + 3 < p.N && (o & 3) == 0) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[i][4 * q], acc[i][4 * q + 1]),
+                                                        pack_bf16x2(acc[i][4 * q + 2], acc[i][4 * q + 3]));
+          } else {
+            for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = f32_to_bf16(acc[i][4 * q + e]);
+          }
+        } else {
+          float* dst = static_cast<float*>(p.out) + o;
+          for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = acc[i][4 * q + e];
+        }
+      }
+    }
+    return;
+  }
+  float* P = p.P + (static_cast<long long>(split) * gridDim.y + g) * p.M * p.N;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int m = m0 + 32 * i + l32;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + 32 * nh + 8 * q + 4 * h;
+      float* dst = P + static_cast<long long>(m) * p.N + n;
+      if (n + 3 < p.N) {
+        *reinterpret_cast<f32x4*>(dst) =
+            f32x4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]};
+      } else {
+        for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = acc[i][4 * q + e];
+      }
+    }
+  }
+}
+
 // One thread per output element (fp32 storage, or shapes the MFMA kernel
 // does not take). Same partial layout as the MFMA kernel.
 template <typename TA, typename TW>
@@ -250,17 +473,28 @@ __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ P
   const int D = d_c + d_R;
   float* red = row + D;
   float ss = 0.f;
+  // Split sums: four independent chains so that the partial loads overlap;
+  // fixed order, hence deterministic.
+  auto split_sum = [&](const float* P, int splits, int width, int c) {
+    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+    const long long stride = static_cast<long long>(M) * width;
+    const float* q = P + static_cast<long long>(m) * width + c;
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+      v0 += q[s * stride];
+      v1 += q[(s + 1) * stride];
+      v2 += q[(s + 2) * stride];
+      v3 += q[(s + 3) * stride];
+    }
+    for (; s < splits; ++s) v0 += q[s * stride];
+    return (v0 + v1) + (v2 + v3);
+  };
   for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < splits_c; ++s) v += Pc[(static_cast<long long>(s) * M + m) * d_c + c];
+    const float v = split_sum(Pc, splits_c, d_c, c);
     row[c] = v;
     ss += v * v;
   }
-  for (int c = threadIdx.x; c < d_R; c += blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < splits_r; ++s) v += Pr[(static_cast<long long>(s) * M + m) * d_R + c];
-    row[d_c + c] = v;
-  }
+  for (int c = threadIdx.x; c < d_R; c += blockDim.x) row[d_c + c] = split_sum(Pr, splits_r, d_R, c);
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -298,6 +532,8 @@ bool mfma_ok(const GemmArgs& a) {
   return true;
 }
 
+bool stream_ok(const GemmArgs& a) { return mfma_ok(a) && !a.w_kn && a.K % SKT == 0 && a.M <= 128; }
+
 int device_cus() {
   static thread_local int dev_cached = -1, cus = 256;
   int dev = 0;
@@ -316,9 +552,15 @@ int gemm_splits(int M, int N, int K, int G, int dtype) {
   (void)dtype;
   const int ksteps = (K + GBK - 1) / GBK;
   const int mblocks = (M + 127) / 128;
-  const long long tiles = static_cast<long long>((N + GBN - 1) / GBN) * G * mblocks;
-  const long long target = 2LL * 256;   // about two workgroups per compute unit
-  long long s = (target + tiles - 1) / tiles;
+  const int nt = stream_nt(N);
+  const long long tiles = static_cast<long long>((N + nt - 1) / nt) * G * mblocks;
+  const long long target = 256;   // about one workgroup per compute unit
+  long long s = target / tiles;   // whole rounds: never spill into a partial second round
+  // Each split writes an fp32 partial of M x N that the epilogue reads back
+  // shortly after (mostly from the last-level cache); keep that traffic
+  // (8*S*M*N bytes) within the weight bytes (2*N*K), i.e. S <= K / (4 M).
+  const long long s_traffic = K / (4LL * (M > 0 ? M : 1));
+  if (s > s_traffic) s = s_traffic;
   if (s > ksteps) s = ksteps;
   if (s < 1) s = 1;
   // k per split is a whole number of steps; recompute the count that covers K
@@ -326,12 +568,38 @@ int gemm_splits(int M, int N, int K, int G, int dtype) {
   return (K + kper - 1) / kper;
 }
 
+bool gemm_direct(const GemmArgs& a) { return a.out != nullptr && a.splits == 1 && stream_ok(a); }
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   const int splits = a.splits;
   const int ksteps = (a.K + GBK - 1) / GBK;
   const int kper = ((ksteps + splits - 1) / splits) * GBK;
+  if (stream_ok(a)) {
+    GemmP p{a.A, a.lda, a.sAg, static_cast<const uint16_t*>(a.W), a.ldw, a.sWg, a.M, a.N, a.K, kper, a.P,
+            nullptr, 0, 0, 0};
+    if (gemm_direct(a)) {
+      p.out = a.out;
+      p.ldo = a.ldo;
+      p.sOg = a.sOg;
+      p.out_bf16 = a.out_dtype == MLA_BF16;
+    }
+    const int MT = a.M <= 32 ? 1 : a.M <= 64 ? 2 : 4;
+    const int nt = stream_nt(a.N);
+    const dim3 grid((a.N + nt - 1) / nt, a.G, splits);
+#define MLA_STREAM(NTV, MTV)                                                                     \
+  if (a.a_f32) gemm_stream_kernel<NTV, MTV, true><<<grid, GTH, 0, stream>>>(p);                  \
+  else gemm_stream_kernel<NTV, MTV, false><<<grid, GTH, 0, stream>>>(p);
+    if (nt == 128) {
+      if (MT == 1) { MLA_STREAM(128, 1) } else if (MT == 2) { MLA_STREAM(128, 2) } else { MLA_STREAM(128, 4) }
+    } else {
+      if (MT == 1) { MLA_STREAM(64, 1) } else if (MT == 2) { MLA_STREAM(64, 2) } else { MLA_STREAM(64, 4) }
+    }
+#undef MLA_STREAM
+    return hipGetLastError();
+  }
   if (mfma_ok(a)) {
-    GemmP p{a.A, a.lda, a.sAg, static_cast<const uint16_t*>(a.W), a.ldw, a.sWg, a.M, a.N, a.K, kper, a.P};
+    GemmP p{a.A, a.lda, a.sAg, static_cast<const uint16_t*>(a.W), a.ldw, a.sWg, a.M, a.N, a.K, kper, a.P,
+            nullptr, 0, 0, 0};
     const int MT = a.M <= 32 ? 1 : a.M <= 64 ? 2 : 4;
     const int mblocks = (a.M + 32 * MT - 1) / (32 * MT);
     const dim3 grid((a.N + GBN - 1) / GBN, a.G, splits * mblocks);

@@ -153,6 +153,22 @@ mla_status gemm(const void* A, long long lda, long long sAg, bool a_f32, const v
   return hip_status(mla::launch_gemm(g, st), "gemm launch");
 }
 
+// Product stored to out[g*sOg + m*ldo + n] in dtype: directly by the GEMM when
+// it runs as one split, else through fp32 partials P and the reduce epilogue.
+mla_status gemm_store(const void* A, long long lda, long long sAg, bool a_f32, const void* W, long long ldw,
+                      long long sWg, bool w_kn, const GemmShape& s, int dtype, float* P, void* out,
+                      long long ldo, long long sOg, hipStream_t st) {
+  mla::GemmArgs g{A, lda, sAg, a_f32, W, ldw, sWg, w_kn, s.M, s.N, s.K, s.G, splits_for(s, dtype), P, dtype};
+  g.out = out;
+  g.ldo = ldo;
+  g.sOg = sOg;
+  g.out_dtype = dtype;
+  if (mla::gemm_direct(g)) return hip_status(mla::launch_gemm(g, st), "gemm launch");
+  g.out = nullptr;
+  MLA_TRY(hip_status(mla::launch_gemm(g, st), "gemm launch"));
+  return hip_status(mla::launch_reduce_store(P, g.splits, s.G, s.M, s.N, out, ldo, sOg, dtype, st), "reduce launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -255,18 +271,14 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const 
   int qin = dims->d;
   if (dims->d_cq) {
     const GemmShape s{B, dims->d_cq, dims->d, 1};
-    MLA_TRY(gemm(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, st));
-    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), 1, B, dims->d_cq, cq, dims->d_cq, 0, dt, st),
-                       "reduce launch"));
+    MLA_TRY(gemm_store(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, cq, dims->d_cq, 0, st));
     cin = cq;
     qin = dims->d_cq;
   }
   // q_C(i) = W_UQ(i) c_Q for all heads at once: W_UQ viewed as [H*d_h][qin]
   {
     const GemmShape s{B, H * d_h, qin, 1};
-    MLA_TRY(gemm(cin, qin, 0, f32, W_UQ, qin, 0, false, s, dt, P, st));
-    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), 1, B, H * d_h, qC, H * d_h, 0, dt, st),
-                       "reduce launch"));
+    MLA_TRY(gemm_store(cin, qin, 0, f32, W_UQ, qin, 0, false, s, dt, P, qC, H * d_h, 0, st));
   }
   // q_R(i) = RoPE(W_QR(i) c_Q, pos) into q[b][i][d_c:]
   {
@@ -281,11 +293,8 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const 
   // W_g(n=c, k) = W_UK[g][k][c] (k-major use of the [d_h][d_c] matrix).
   {
     const GemmShape s{B, d_c, d_h, H};
-    MLA_TRY(gemm(qC, static_cast<long long>(H) * d_h, d_h, f32, W_UK, d_c, static_cast<long long>(d_h) * d_c,
-                 true, s, dt, P, st));
-    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), H, B, d_c, q, static_cast<long long>(H) * D,
-                                                D, dt, st),
-                       "reduce launch"));
+    MLA_TRY(gemm_store(qC, static_cast<long long>(H) * d_h, d_h, f32, W_UK, d_c, static_cast<long long>(d_h) * d_c,
+                       true, s, dt, P, q, static_cast<long long>(H) * D, D, st));
   }
   return ok();
 }
@@ -368,18 +377,13 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat, con
   {
     // o_heads(b,i) = W_UV(i) o_lat(b,i): per head g, A_g[b][c] = o_lat[b][g][c]
     const GemmShape s{B, d_v, d_c, H};
-    MLA_TRY(gemm(o_lat, static_cast<long long>(H) * d_c, d_c, true, W_UV, d_c, static_cast<long long>(d_v) * d_c,
-                 false, s, dt, P, st));
-    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), H, B, d_v, o_heads,
-                                                static_cast<long long>(H) * d_v, d_v, dt, st),
-                       "reduce launch"));
+    MLA_TRY(gemm_store(o_lat, static_cast<long long>(H) * d_c, d_c, true, W_UV, d_c, static_cast<long long>(d_v) * d_c,
+                       false, s, dt, P, o_heads, static_cast<long long>(H) * d_v, d_v, st));
   }
   if (W_O) {
     const GemmShape s{B, dims->d, H * d_v, 1};
-    MLA_TRY(gemm(o_heads, static_cast<long long>(H) * d_v, 0, f32, W_O, static_cast<long long>(H) * d_v, 0, false, s,
-                 dt, P, st));
-    MLA_TRY(hip_status(mla::launch_reduce_store(P, splits_for(s, dt), 1, B, dims->d, out, dims->d, 0, dt, st),
-                       "reduce launch"));
+    MLA_TRY(gemm_store(o_heads, static_cast<long long>(H) * d_v, 0, f32, W_O, static_cast<long long>(H) * d_v, 0,
+                       false, s, dt, P, out, dims->d, 0, st));
   }
   return ok();
 }

@@ -67,8 +67,16 @@ struct GemmArgs {
   int splits;                 // k splits (>= 1)
   float* P;                   // [splits][G][M][N] fp32
   int dtype;                  // storage dtype of W (and of A unless a_f32)
+  // Optional direct store (taken when gemm_direct() says so): the product is
+  // written to out[g*sOg + m*ldo + n] in out_dtype instead of partials P.
+  void* out = nullptr;
+  long long ldo = 0, sOg = 0;
+  int out_dtype = 0;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// True when launch_gemm stores a's product directly to a.out (one split on
+// the streaming kernel); otherwise it writes partials for an epilogue.
+bool gemm_direct(const GemmArgs& a);
 // Number of k splits launch_gemm would pick for a shape (used to size workspaces).
 int gemm_splits(int M, int N, int K, int G, int dtype);
 
