@@ -234,7 +234,9 @@ __device__ __forceinline__ void copy_part(const TileCopy& c, int k, uint32_t lat
   }
 }
 
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Workgroup barrier; this wave's LDS writes (the softmax weights) complete
+// first, so that every wave reads them after the barrier.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Keeps a value in a register at this point of the instruction stream: the
 // computation producing it cannot sink below, nor its users rise above, the

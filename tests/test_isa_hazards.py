@@ -7,7 +7,9 @@ wait states. This test compiles the kernel to assembly (CPU only, hipcc
 cross-compiles for gfx950) and scans it in program order:
 
   * a VALU instruction that writes a VGPR which a following MFMA reads must
-    be at least MIN_VALU_TO_MFMA wait states before that MFMA;
+    be at least MIN_VALU_TO_MFMA wait states before that MFMA, unless a
+    memory load overwrites the register in between (the MFMA then reads the
+    load's data, which the memory counter waits cover);
   * an MFMA result in VGPRs must not be read by a VALU instruction within
     MIN_MFMA_TO_VALU wait states; an MFMA result in AGPRs must not be read by
     v_accvgpr_read within the same distance.
@@ -91,15 +93,19 @@ def test_valu_writes_before_mfma_reads(kernels):
             dist = 0
             for j in range(i - 1, max(-1, i - 40), -1):
                 prev = insts[j]
-                if prev.startswith("v_") and not prev.startswith("v_mfma") and \
+                dst = prev.split(None, 1)[1].split(",")[0].strip() if " " in prev else ""
+                f, regs = _regs(dst)
+                if prev.startswith(("ds_read", "global_load", "buffer_load")) and f == "v":
+                    # a later load overwrites these registers: their last
+                    # writer is the load, covered by the memory counters
+                    srcs -= regs
+                elif prev.startswith("v_") and not prev.startswith("v_mfma") and \
                         not prev.startswith("v_accvgpr_write"):
-                    dst = prev.split(None, 1)[1].split(",")[0].strip() if " " in prev else ""
-                    f, regs = _regs(dst)
                     if f == "v" and regs & srcs:
                         assert dist >= MIN_VALU_TO_MFMA, (name, i, prev, ins, dist)
                         break
                 dist += _wait_states(prev)
-                if dist >= MIN_VALU_TO_MFMA:
+                if dist >= MIN_VALU_TO_MFMA or not srcs:
                     break
 
 
