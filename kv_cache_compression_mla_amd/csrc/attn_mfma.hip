@@ -108,13 +108,145 @@ struct Params {
   long long seq_stride;   // contiguous: capacity * DW elements
   int bs_log2, max_blocks;
   const int32_t* __restrict__ seq_lens;
-  int H, chunk, splits;
+  int B, H;
+  int grid;               // workgroups launched (>= chunks in the plan)
+  int splits;             // > 0: chunks per sequence (at most); 0: balanced plan
   float sl2;              // softmax scale * log2(e)
   float* o_lat;
   float* lse;
-  float* part_o;
-  float* part_ml;
+  float* part_o;          // [grid][H][512] partials, by chunk
+  float* part_ml;         // [grid][H][2]
+  int2* plan_seq;         // [B]: (first chunk, chunks) of each sequence
 };
+
+// ---- chunk plan ----
+// The rows of every sequence are cut into chunks of whole 32-row tiles, one
+// chunk per workgroup; a sequence with more than one chunk gets (m, l, O)
+// partials, merged by combine_chunks. Every workgroup computes the same plan
+// from seq_lens (wave 0, in registers and LDS scratch) and finds its own
+// chunk in it.
+//  * splits > 0: sequence b gets ceil(L_b / c_b) chunks of c_b rows, c_b =
+//    the multiple of 32 at or above L_b / splits.
+//  * splits = 0 (balanced): the smallest chunk size C (a multiple of 32, at
+//    least MIN_CHUNK rows) for which the chunk count sum_b ceil(L_b / C) fits
+//    the grid; then sequence b gets ceil(L_b / C) chunks of near-equal size.
+//    Long and short sequences of a ragged batch thus finish together, and a
+//    batch of equal lengths gets ceil(L / C) chunks each.
+// A sequence of length 0 gets one empty chunk (output: zeros, lse -inf).
+constexpr int MIN_CHUNK = 256;
+struct ChunkPlan {
+  int b, r0, r1;   // sequence and rows [r0, r1)
+  int start, n;    // the sequence's chunks: [start, start + n)
+  int total;       // chunks in the plan (workgroups past it have no work)
+};
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ long long wave_sum64(long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int lo = __shfl_xor(static_cast<int>(v & 0xffffffffLL), o);
+    const int hi = __shfl_xor(static_cast<int>(v >> 32), o);
+    v += (static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo);
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Chunks of one sequence of length L, given its target count t >= 1.
+__device__ __forceinline__ void seq_chunks(int L, int t, int* rows, int* n) {
+  const int c = max(TILE, ceil_div(ceil_div(L, t), TILE) * TILE);
+  *rows = c;
+  *n = max(1, ceil_div(L, c));
+}
+
+// Every thread of the workgroup calls this; the result is the same in all.
+// scratch: LDS for B ints (free until the first tile copy); res: 8 ints of
+// LDS that stay untouched until the epilogue.
+__device__ ChunkPlan plan_chunks(const Params& p, int* scratch, int* res) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int lane = tid;
+    for (int i = lane; i < p.B; i += 64) scratch[i] = p.seq_lens[i];
+    // (LDS writes and reads below are by this wave only, in order)
+    int target_rows = 0;   // balanced: the chunk size C
+    if (p.splits == 0) {
+      long long sum = 0;
+      int mx = 0;
+      for (int i = lane; i < p.B; i += 64) {
+        sum += scratch[i];
+        mx = max(mx, scratch[i]);
+      }
+      sum = wave_sum64(sum);
+      mx = wave_max(mx);
+      const int avg = static_cast<int>((sum + p.grid - 1) / p.grid);
+      int klo = ceil_div(max(MIN_CHUNK, avg), TILE);
+      int khi = max(klo, ceil_div(max(mx, 1), TILE));
+      while (klo < khi) {   // smallest k with sum_b max(1, ceil(L_b / 32k)) <= grid
+        const int mid = (klo + khi) >> 1, c = mid * TILE;
+        int cnt = 0;
+        for (int i = lane; i < p.B; i += 64) cnt += max(1, ceil_div(scratch[i], c));
+        if (wave_sum(cnt) <= p.grid) khi = mid;
+        else klo = mid + 1;
+      }
+      target_rows = klo * TILE;
+    }
+    // chunk counts, then an exclusive scan over the sequences in lane-major
+    // blocks: lane l owns sequences [l * per, (l + 1) * per)
+    const int per = ceil_div(p.B, 64);
+    int local = 0;
+    for (int i = lane * per; i < min(p.B, (lane + 1) * per); ++i) {
+      const int L = scratch[i];
+      int rows, n;
+      seq_chunks(L, p.splits > 0 ? p.splits : max(1, ceil_div(L, target_rows)), &rows, &n);
+      local += n;
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    const int total = __shfl(incl, 63);
+    int start = incl - local;
+    const int g = blockIdx.x;
+    for (int i = lane * per; i < min(p.B, (lane + 1) * per); ++i) {
+      const int L = scratch[i];
+      int rows, n;
+      seq_chunks(L, p.splits > 0 ? p.splits : max(1, ceil_div(L, target_rows)), &rows, &n);
+      if (g >= start && g < start + n) {
+        const int k = g - start;
+        res[0] = i;
+        res[1] = k * rows;
+        res[2] = min((k + 1) * rows, L);
+        res[3] = start;
+        res[4] = n;
+      }
+      start += n;
+    }
+    if (lane == 0) {
+      res[5] = total;
+      if (g >= total) res[0] = -1;
+    }
+  }
+  __syncthreads();
+  ChunkPlan c;
+  c.b = __builtin_amdgcn_readfirstlane(res[0]);
+  c.r0 = __builtin_amdgcn_readfirstlane(res[1]);
+  c.r1 = __builtin_amdgcn_readfirstlane(res[2]);
+  c.start = __builtin_amdgcn_readfirstlane(res[3]);
+  c.n = __builtin_amdgcn_readfirstlane(res[4]);
+  c.total = __builtin_amdgcn_readfirstlane(res[5]);
+  return c;
+}
 
 // XOR swizzle of the 16-byte chunks of a packed 128-byte rotary row: 16
 // lanes reading one chunk of 16 rows hit distinct bank groups.
@@ -296,19 +428,21 @@ void attn_mfma_kernel(Params p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int s_idx = blockIdx.x % p.splits;
-  const int b = blockIdx.x / p.splits;
   const int hq = w % NW;              // this wave's score head block
   const int qhead = 32 * hq + l32;    // this lane's score head
 
-  const int L = p.seq_lens[b];
-  const int row_begin = s_idx * p.chunk;
-  const int row_end = min(row_begin + p.chunk, L);
+  const ChunkPlan plan = plan_chunks(p, reinterpret_cast<int*>(smem), reinterpret_cast<int*>(smem + LM_OFF));
+  if (plan.b < 0) return;             // no chunk for this workgroup
+  const int b = plan.b;
+  const int gi = blockIdx.x;          // chunk index (partials)
+  const bool single = plan.n == 1;    // whole sequence here: final output
+  if (tid == 0 && plan.r0 == 0) p.plan_seq[b] = int2{plan.start, plan.n};
+  const int row_begin = plan.r0;
+  const int row_end = plan.r1;
 
   if (row_begin >= row_end) {
-    // Nothing to attend in this chunk. With splits > 1 the combine kernel
-    // skips it; with a single split the sequence is empty: zeros, lse -inf.
-    if (p.splits == 1 && w < NW) {
+    // Empty sequence (its single chunk): zeros, lse -inf.
+    if (w < NW) {
       float* o = p.o_lat + (static_cast<long long>(b) * p.H + qhead) * DC;
       for (int c = h * 256; c < h * 256 + 256; c += 4)
         *reinterpret_cast<f32x4*>(o + c) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -592,10 +726,10 @@ void attn_mfma_kernel(Params p) {
   if (w < NW && h == 0) {
     lm[2 * qhead] = m_ref;
     lm[2 * qhead + 1] = l_tot;
-    if (p.splits == 1) {
+    if (single) {
       if (p.lse) p.lse[b * p.H + qhead] = (m_ref + log2f(l_tot)) * 0.69314718055994531f;
     } else {
-      const long long pidx = (static_cast<long long>(b) * p.splits + s_idx) * p.H + qhead;
+      const long long pidx = static_cast<long long>(gi) * p.H + qhead;
       p.part_ml[pidx * 2] = m_ref;
       p.part_ml[pidx * 2 + 1] = l_tot;
     }
@@ -608,10 +742,9 @@ void attn_mfma_kernel(Params p) {
 #pragma unroll
   for (int hb = 0; hb < NW; ++hb) {
     const int head = 32 * hb + l32;
-    const float inv = (p.splits == 1) ? 1.f / lm[2 * head + 1] : 1.f;
-    float* o = (p.splits == 1)
-                   ? p.o_lat + (static_cast<long long>(b) * p.H + head) * DC
-                   : p.part_o + ((static_cast<long long>(b) * p.splits + s_idx) * p.H + head) * DC;
+    const float inv = single ? 1.f / lm[2 * head + 1] : 1.f;
+    float* o = single ? p.o_lat + (static_cast<long long>(b) * p.H + head) * DC
+                      : p.part_o + (static_cast<long long>(gi) * p.H + head) * DC;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float x[16];
@@ -620,11 +753,75 @@ void attn_mfma_kernel(Params p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = colbase(4 * w + c) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
+        // plain stores: these 16-byte pieces of 32 head rows complete their
+        // lines across the wave's stores, in L2
         *reinterpret_cast<f32x4*>(o + col) =
             f32x4{x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv};
       }
     }
   }
+}
+
+// Exact merge of the chunk partials of one (b, head), for sequences with
+// more than one chunk: M = max m_j, w_j = 2^(m_j - M),
+// o = sum_j w_j O_j / sum_j w_j l_j and lse = (M + log2 sum_j w_j l_j) ln 2.
+// Up to 64 chunks, lane j of each wave reads (m, l) of chunk j, so the
+// maximum, weights and denominator come from wave reductions; every thread
+// streams 4 columns of every partial once, groups of GRP loads issued before
+// their weights are needed (padding loads re-read the last partial and weigh
+// 0). More chunks take a plain loop.
+__global__ __launch_bounds__(128) void combine_chunks(Params p) {
+  const int head = blockIdx.x % p.H;
+  const int b = blockIdx.x / p.H;
+  const int2 pl = p.plan_seq[b];
+  const int start = pl.x, n = pl.y;
+  if (n <= 1) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int GRP = 4;
+  const long long so = static_cast<long long>(p.H) * DC;   // partial stride (floats)
+  const long long sm = 2LL * p.H;
+  const float* po = p.part_o + (static_cast<long long>(start) * p.H + head) * DC + 4 * threadIdx.x;
+  const float* pm = p.part_ml + (static_cast<long long>(start) * p.H + head) * 2;
+  auto load = [&](int j) { return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + j * so)); };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY, den = 0.f;
+  if (n <= 64) {
+    f32x4 v0 = load(0), v1 = load(1), v2 = load(min(2, n - 1)), v3 = load(min(3, n - 1));
+    const float m = lane < n ? pm[lane * sm] : -INFINITY;
+    const float l = lane < n ? pm[lane * sm + 1] : 0.f;
+    M = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float w = lane < n ? exp2f(m - M) : 0.f;
+    den = w * l;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+    for (int j = 0; j < n; j += GRP) {
+      if (j > 0) {
+        v0 = load(j);
+        v1 = load(min(j + 1, n - 1));
+        v2 = load(min(j + 2, n - 1));
+        v3 = load(min(j + 3, n - 1));
+      }
+      acc += __shfl(w, j) * v0;
+      acc += __shfl(w, min(j + 1, 63)) * (j + 1 < n ? v1 : f32x4{0.f, 0.f, 0.f, 0.f});
+      acc += __shfl(w, min(j + 2, 63)) * (j + 2 < n ? v2 : f32x4{0.f, 0.f, 0.f, 0.f});
+      acc += __shfl(w, min(j + 3, 63)) * (j + 3 < n ? v3 : f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+  } else {
+    for (int j = 0; j < n; ++j) M = fmaxf(M, pm[j * sm]);
+    for (int j = 0; j < n; ++j) {
+      const float w = exp2f(pm[j * sm] - M);
+      den += w * pm[j * sm + 1];
+      acc += w * load(j);
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  __builtin_nontemporal_store(acc * inv,
+                              reinterpret_cast<f32x4*>(p.o_lat + (static_cast<long long>(b) * p.H + head) * DC +
+                                                       4 * threadIdx.x));
+  if (p.lse && threadIdx.x == 0)
+    p.lse[b * p.H + head] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace
@@ -638,15 +835,17 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
   p.bs_log2 = a.block_table ? __builtin_ctz(static_cast<unsigned>(a.block_size)) : 0;
   p.max_blocks = a.max_blocks;
   p.seq_lens = a.seq_lens;
+  p.B = a.B;
   p.H = a.H;
-  p.chunk = a.chunk;
+  p.grid = a.grid;
   p.splits = a.splits;
   p.sl2 = a.scale * 1.4426950408889634f;
   p.o_lat = a.o_lat;
   p.lse = a.lse;
   p.part_o = a.part_o;
   p.part_ml = a.part_ml;
-  const dim3 grid(a.B * a.splits);
+  p.plan_seq = a.plan_seq;
+  const dim3 grid(a.grid);
   const int pm = !a.block_table ? CONTIG : (a.block_size >= 8 ? PAGED8 : PAGED_SMALL);
 #define MLA_ATTN_LAUNCH(NW)                                                               \
   if (pm == CONTIG) attn_mfma_kernel<NW, CONTIG><<<grid, NTHREADS, 0, stream>>>(p);       \
@@ -660,6 +859,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
 #undef MLA_ATTN_LAUNCH
+  // with one workgroup per sequence every sequence has a single chunk
+  if (a.grid > a.B) combine_chunks<<<dim3(a.B * a.H), 128, 0, stream>>>(p);
   return hipGetLastError();
 }
 

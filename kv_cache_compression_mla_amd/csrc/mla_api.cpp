@@ -80,7 +80,40 @@ bool mfma_attn(const mla_dims* d) {
   return d->dtype == MLA_BF16 && d->d_c == 512 && d->d_R == 64 && d->H % 32 == 0 && d->H <= 128;
 }
 
-// Split count and rows per split for the attention launch.
+// MFMA attention: workgroups launched. Explicit splits: num_splits per
+// sequence (at most); balanced plan: one per compute unit, at least one per
+// sequence. The device cuts the sequences into chunks that fit this grid.
+constexpr int kMaxMfmaBatch = 32768;   // plan scratch: B ints of LDS
+constexpr int kMinChunk = 256;         // rows; the device plan's lower bound on the chunk size
+int cdiv(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
+// explicit split count, clamped to the tiles of the longest sequence (more
+// would give the same chunks); 0 = balanced plan
+int mfma_splits(int num_splits, int max_seq_len) {
+  return num_splits > 0 ? std::min(num_splits, std::max(1, cdiv(max_seq_len, 32))) : 0;
+}
+long long mfma_grid(int B, int splits) {
+  return splits > 0 ? static_cast<long long>(B) * splits : std::max(device_cus(), B);
+}
+constexpr long long kMaxMfmaGrid = 1LL << 22;
+// Chunks the device plan gives a sequence of length L when all B sequences
+// have that length (the plan itself runs on the device from seq_lens).
+int mfma_uniform_chunks(int B, int L, int num_splits, int grid) {
+  auto chunks = [&](int t) {
+    const int c = std::max(32, cdiv(cdiv(L, t), 32) * 32);
+    return std::max(1, cdiv(L, c));
+  };
+  if (num_splits > 0) return chunks(num_splits);
+  int klo = cdiv(std::max(kMinChunk, cdiv(std::max(static_cast<long long>(B) * L, 1LL), grid)), 32);
+  int khi = std::max(klo, cdiv(std::max(L, 1), 32));
+  while (klo < khi) {
+    const int mid = (klo + khi) / 2;
+    if (static_cast<long long>(B) * std::max(1, cdiv(L, mid * 32)) <= grid) khi = mid;
+    else klo = mid + 1;
+  }
+  return chunks(std::max(1, cdiv(L, klo * 32)));
+}
+
+// Split count and rows per split for the generic attention launch.
 void attn_plan(const mla_dims* d, int B, int max_seq_len, int num_splits, int* splits, int* chunk) {
   const int L = max_seq_len > 0 ? max_seq_len : 1;
   int s = num_splits;
@@ -123,7 +156,15 @@ size_t ws_absorb(const mla_dims* d, int B) {
          align_up(p);
 }
 
+// MFMA path: partial (O, m, l) per chunk of the grid, then the plan's
+// per-sequence (first chunk, chunks).
+size_t ws_attn_mfma(const mla_dims* d, int B, int max_seq_len, int num_splits) {
+  const size_t g = static_cast<size_t>(std::min(kMaxMfmaGrid, mfma_grid(B, mfma_splits(num_splits, max_seq_len))));
+  return align_up(g * d->H * d->d_c * sizeof(float)) + align_up(g * d->H * 2 * sizeof(float)) +
+         align_up(static_cast<size_t>(B) * 2 * sizeof(int));
+}
 size_t ws_attn(const mla_dims* d, int B, int max_seq_len, int num_splits) {
+  if (mfma_attn(d)) return ws_attn_mfma(d, B, max_seq_len, num_splits);
   int s = 1, ch = 1;
   attn_plan(d, B, max_seq_len, num_splits, &s, &ch);
   if (s <= 1) return 0;
@@ -201,6 +242,10 @@ int32_t mla_decode_kernel(const mla_dims* dims) {
 
 int32_t mla_decode_num_splits(const mla_dims* dims, int32_t B, int32_t max_seq_len, int32_t num_splits) {
   if (check_dims(dims) != MLA_OK || B <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  if (mfma_attn(dims)) {
+    const int s = mfma_splits(num_splits, max_seq_len);
+    return mfma_uniform_chunks(B, max_seq_len, s, static_cast<int>(std::min(kMaxMfmaGrid, mfma_grid(B, s))));
+  }
   int s = 1, ch = 1;
   attn_plan(dims, B, max_seq_len, num_splits, &s, &ch);
   return s;
@@ -314,6 +359,10 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const
     return fail(MLA_ERR_SHAPE, "max_seq_len exceeds max_blocks * block_size");
   for (const void* p : {q, static_cast<const void*>(seq_lens), static_cast<const void*>(o_lat)})
     if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "decode_attn: pointer not 16-byte aligned");
+  const bool mfma = mfma_attn(dims);
+  if (mfma && B > kMaxMfmaBatch) return fail(MLA_ERR_UNSUPPORTED, "decode_attn: B above %d", kMaxMfmaBatch);
+  if (mfma && mfma_grid(B, mfma_splits(num_splits, max_seq_len)) > kMaxMfmaGrid)
+    return fail(MLA_ERR_UNSUPPORTED, "decode_attn: B * num_splits above %lld", kMaxMfmaGrid);
   int splits = 1, chunk = 1;
   attn_plan(dims, B, max_seq_len, num_splits, &splits, &chunk);
   const size_t need = ws_attn(dims, B, max_seq_len, num_splits);
@@ -338,6 +387,21 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const
   a.o_lat = o_lat;
   a.lse = lse;
   a.dtype = dims->dtype;
+  if (mfma) {
+    // the device plans the chunks (balanced when num_splits is 0) and merges them
+    const int s = mfma_splits(num_splits, max_seq_len);
+    const size_t g = static_cast<size_t>(mfma_grid(B, s));
+    char* w = static_cast<char*>(ws);
+    a.splits = s;
+    a.grid = static_cast<int>(g);
+    a.part_o = reinterpret_cast<float*>(w);
+    w += align_up(g * dims->H * dims->d_c * sizeof(float));
+    a.part_ml = reinterpret_cast<float*>(w);
+    w += align_up(g * dims->H * 2 * sizeof(float));
+    a.plan_seq = reinterpret_cast<int2*>(w);
+    MLA_TRY(hip_status(mla::launch_attn_mfma(a, st), "attention launch"));
+    return ok();
+  }
   if (splits > 1) {
     a.part_o = static_cast<float*>(ws);
     a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -348,11 +412,7 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const
     a.splits = 1;
     a.chunk = 1;
   }
-  if (mfma_attn(dims)) {
-    MLA_TRY(hip_status(mla::launch_attn_mfma(a, st), "attention launch"));
-  } else {
-    MLA_TRY(hip_status(mla::launch_attn_generic(a, st), "attention launch"));
-  }
+  MLA_TRY(hip_status(mla::launch_attn_generic(a, st), "attention launch"));
   if (a.splits > 1) MLA_TRY(hip_status(mla::launch_attn_combine(a, st), "combine launch"));
   return ok();
 }

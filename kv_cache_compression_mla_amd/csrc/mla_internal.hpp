@@ -111,9 +111,13 @@ struct AttnArgs {
   float scale;
   float* o_lat;
   float* lse;
-  float* part_o;    // [B][splits][H][d_c]
-  float* part_ml;   // [B][splits][H][2]
+  float* part_o;    // generic: [B][splits][H][d_c]; MFMA: [grid][H][d_c], by chunk
+  float* part_ml;   // generic: [B][splits][H][2];   MFMA: [grid][H][2]
   int dtype;
+  // MFMA kernel: workgroups launched, and per sequence (first chunk, chunks)
+  // of the plan it computes on the device (splits = 0: balanced plan)
+  int grid = 0;
+  int2* plan_seq = nullptr;
 };
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream);

@@ -1,0 +1,105 @@
+"""The attention chunk plan: how sequences are cut into per-workgroup chunks.
+
+The plan runs on the device (every attention workgroup computes it from
+seq_lens). These CPU tests restate it in Python and check the properties the
+kernel and the combine rely on: every row of every sequence lies in exactly one
+chunk, chunks are whole 32-row tiles except at a sequence's end, the chunk count
+fits the grid, a sequence of length 0 gets one empty chunk, and the balanced
+plan's largest chunk is the smallest the grid allows. They also check that the
+library's host-side split count (mla_decode_num_splits, which models a batch of
+equal lengths) agrees with the restated plan.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from kv_cache_compression_mla_amd import mla
+
+TILE, MIN_CHUNK, CUS = 32, 256, 256
+
+
+def seq_chunks(L, t):
+    c = max(TILE, -(-(-(-L // t)) // TILE) * TILE)
+    return c, max(1, -(-L // c))
+
+
+def plan(lens, splits, grid):
+    """(chunk size C of the balanced plan or None, [(b, r0, r1)] by chunk index)."""
+    C = None
+    if splits == 0:
+        total = max(int(sum(lens)), 1)
+        klo = -(-max(MIN_CHUNK, -(-total // grid)) // TILE)
+        khi = max(klo, -(-max(max(lens), 1) // TILE))
+        while klo < khi:
+            mid = (klo + khi) // 2
+            if sum(max(1, -(-L // (mid * TILE))) for L in lens) <= grid:
+                khi = mid
+            else:
+                klo = mid + 1
+        C = klo * TILE
+    chunks = []
+    for b, L in enumerate(lens):
+        rows, n = seq_chunks(L, splits if splits > 0 else max(1, -(-L // C)))
+        chunks += [(b, k * rows, min((k + 1) * rows, L)) for k in range(n)]
+    return C, chunks
+
+
+def check(lens, splits, grid):
+    C, chunks = plan(lens, splits, grid)
+    assert len(chunks) <= grid
+    for b, L in enumerate(lens):
+        mine = [(r0, r1) for bb, r0, r1 in chunks if bb == b]
+        assert mine, b
+        if L == 0:
+            assert mine == [(0, 0)]
+            continue
+        assert mine[0][0] == 0 and mine[-1][1] == L
+        for (a0, a1), (c0, c1) in zip(mine, mine[1:]):
+            assert a1 == c0 and a0 % TILE == 0 and a1 % TILE == 0
+        assert all(r1 > r0 for r0, r1 in mine)
+        if splits > 0:
+            assert len(mine) <= splits
+    return C, chunks
+
+
+def test_equal_lengths_give_the_even_split():
+    # B = 64 x 8193 rows: four chunks of 2080 rows each, 256 workgroups
+    C, chunks = check([8193] * 64, 0, CUS)
+    assert C == 2080 and len(chunks) == 256
+    # B = 8 x 32769: 32 chunks of 1056 rows
+    C, chunks = check([32769] * 8, 0, CUS)
+    assert C == 1056 and len(chunks) == 256
+
+
+def test_ragged_batch_is_balanced():
+    rng = np.random.default_rng(0)
+    lens = [int(x) + 1 for x in rng.integers(1024, 16385, size=128)]
+    C, chunks = check(lens, 0, CUS)
+    longest = max(r1 - r0 for _, r0, r1 in chunks)
+    # no smaller chunk size fits the grid
+    assert sum(max(1, math.ceil(L / (C - TILE))) for L in lens) > CUS
+    # far below a fixed two-way split of the longest sequence
+    assert longest <= C < max(lens) // 2 + TILE
+
+
+def test_short_sequences_and_empty_ones():
+    for lens in ([0], [0, 0, 5], [1, 31, 32, 33], [517, 96], [4097], [1] * 300):
+        for splits in (0, 1, 2, 3, 5, 7):
+            check(lens, splits, len(lens) * splits if splits else max(CUS, len(lens)))
+
+
+def test_min_chunk_bounds_partial_traffic():
+    # one sequence of 4097 rows: chunks of at least 256 rows
+    C, chunks = check([4097], 0, CUS)
+    assert C == MIN_CHUNK and len(chunks) == 17
+
+
+@pytest.mark.parametrize("B,L,splits", [(64, 8193, 0), (8, 32769, 0), (1, 4097, 0), (64, 8193, 4),
+                                        (8, 32769, 32), (2, 1500, 7), (3, 300, 0), (128, 100, 0), (512, 8193, 0)])
+def test_host_split_count_matches_the_plan(B, L, splits):
+    d = mla.make_dims(7168, 128, 128, 128, 512, 64, 1536, "bf16")
+    s = min(splits, max(1, -(-L // TILE))) if splits else 0
+    grid = B * s if s else max(CUS, B)
+    _, chunks = plan([L] * B, s, grid)
+    assert mla.decode_num_splits(d, B, L, splits) == sum(1 for b, _, _ in chunks if b == 0)
