@@ -148,9 +148,20 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t,
  *   seq_lens   [B] int32 device: rows attended, the new token included; 0 gives
  *              an all-zero o_lat row and lse = -inf
  *   max_seq_len host upper bound of seq_lens (sizes the launch)
- *   num_splits context splits per sequence, 0 = automatic; the context is cut
- *              into equal chunks and merged exactly afterwards
+ *   num_splits context chunks per sequence (at most), 0 = automatic. Each
+ *              chunk is a run of whole 32-row tiles handled by one
+ *              workgroup; the chunks of a sequence are merged exactly
+ *              afterwards. Automatic (bf16 MFMA path, the V3 geometry): the
+ *              device reads seq_lens and picks the smallest chunk size (at
+ *              least 256 rows) whose chunk count fits one workgroup per
+ *              compute unit (or per sequence, if B is larger), so a ragged
+ *              batch is balanced. Other geometries cut every sequence into
+ *              the same number of equal chunks of max_seq_len.
  *   o_lat      [B][H][d_c] float32 out;  lse [B][H] float32 out, or NULL
+ *   ws         workspace of at least mla_workspace_bytes(dims, B, max_seq_len,
+ *              num_splits) bytes: chunk partials and the chunk plan
+ * Errors: MLA_ERR_UNSUPPORTED if B exceeds 32768 or B * num_splits exceeds
+ * 2^22 on the MFMA path.
  */
 mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q,
                            const mla_cache* cache, const int32_t* seq_lens,
@@ -175,8 +186,10 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat,
 size_t mla_workspace_bytes(const mla_dims* dims, int32_t B, int32_t max_seq_len,
                            int32_t num_splits);
 
-/* The split count mla_decode_attn will use (resolves 0 = automatic); 0 on
- * bad dims. Needs the current device's compute-unit count for the automatic
+/* The number of chunks mla_decode_attn gives a sequence of max_seq_len rows
+ * when all B sequences have that length (resolves 0 = automatic; with ragged
+ * lengths the automatic plan is made on the device from seq_lens); 0 on bad
+ * dims. Needs the current device's compute-unit count for the automatic
  * choice. */
 int32_t mla_decode_num_splits(const mla_dims* dims, int32_t B, int32_t max_seq_len,
                               int32_t num_splits);
