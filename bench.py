@@ -170,7 +170,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "mla_decode_attn call (attn_mfma_kernel + attn_combine_kernel)",
+                     "kernel": "mla_decode_attn call (attn_mfma_kernel + combine_chunks)",
                      "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:

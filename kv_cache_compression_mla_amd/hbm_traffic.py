@@ -34,7 +34,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ATTN_SRC = os.path.join(ROOT, "kv_cache_compression_mla_amd", "csrc", "attn_mfma.hip")
 COPY_BYTES = 256 << 20
-KERNELS = {"attn": "attn_mfma_kernel", "combine": "attn_combine_kernel", "copy": "MulFunctor",
+KERNELS = {"attn": "attn_mfma_kernel", "combine": "combine_chunks", "copy": "MulFunctor",
            "fill": "FillFunctor", "sum": "reduce_kernel", "blit": "copyBuffer"}
 
 
