@@ -31,6 +31,8 @@ __device__ __forceinline__ int gslot(int r, int kc) { return r * 8 + (kc ^ ((r >
 struct GemmP {
   const void* A; long long lda, sAg;
   const uint16_t* W; long long ldw, sWg;
+  const uint16_t* W2;     // columns n >= n_split come from W2 row n - n_split (or NULL)
+  int n_split;
   int M, N, K, ksplit;    // ksplit = k per split (multiple of GBK)
   float* P;
   void* out;              // direct store (streaming kernel, one split) or NULL
@@ -154,6 +156,33 @@ __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
     }
   }
   // D[n][m]: lane holds m = 32i + l32, n = 32w + 8(r/4) + 4h + r%4.
+  if (p.out) {
+    // one split: store the product itself, out[g*sOg + m*ldo + n]
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + 32 * i + l32;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 32 * w + 8 * q + 4 * h;
+        const long long o = g * p.sOg + static_cast<long long>(m) * p.ldo + n;
+        if (p.out_bf16) {
+          uint16_t* dst = static_cast<uint16_t*>(p.out) + o;
+          if (n + 3 < p.N) {
+            *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(acc[i][4 * q], acc[i][4 * q + 1]),
+                                                   pack_bf16x2(acc[i][4 * q + 2], acc[i][4 * q + 3])};
+          } else {
+            for (int e = 0; e < 4 && n + e < p.N; ++e)
+              dst[e] = static_cast<uint16_t>(pack_bf16x2(acc[i][4 * q + e], 0.f) & 0xffffu);
+          }
+        } else {
+          float* dst = static_cast<float*>(p.out) + o;
+          for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = acc[i][4 * q + e];
+        }
+      }
+    }
+    return;
+  }
   float* P = p.P + (static_cast<long long>(split) * gridDim.y + g) * p.M * p.N;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
@@ -191,7 +220,9 @@ __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
 // ---------------------------------------------------------------------------
 // weight rows per workgroup: 128 for wide outputs (halves the activation
 // re-reads), 64 otherwise (more workgroups on narrow outputs)
-__host__ __device__ constexpr int stream_nt(int N) { return N >= 4096 ? 128 : 64; }
+// (very wide outputs go back to 64 so that one k split already fills the
+// chip and the product is stored directly)
+__host__ __device__ constexpr int stream_nt(int N) { return (N >= 4096 && N < 12288) ? 128 : 64; }
 constexpr int SKT = 64;      // k per stage
 
 template <int N>
@@ -258,7 +289,10 @@ __global__ __launch_bounds__(GTH) void gemm_stream_kernel(GemmP p) {
   const int k_begin = split * p.ksplit;
   const int k_end = min(p.K, k_begin + p.ksplit);
   const int nsteps = k_end > k_begin ? (k_end - k_begin) / SKT : 0;
-  const uint16_t* W = p.W + g * p.sWg;
+  // a tile lies wholly on one side of n_split (a multiple of NT)
+  const bool second = p.W2 != nullptr && n0 >= p.n_split;
+  const uint16_t* W = second ? p.W2 : p.W + g * p.sWg;
+  const int wrow0 = second ? p.n_split : 0;
 
   // copy i of a stage (0..COPIES-1) for this lane: source address and LDS offset
   auto issue_stage = [&](int t) {
@@ -270,7 +304,7 @@ __global__ __launch_bounds__(GTH) void gemm_stream_kernel(GemmP p) {
       if (i < NT / 8) {                              // weight rows 8i..8i+7
         const int r = 8 * i + (lane >> 3), slot = lane & 7;
         const int c = slot ^ ((r >> 1) & 7);
-        const int n = min(n0 + r, p.N - 1);
+        const int n = min(n0 + r, p.N - 1) - wrow0;
         dma_copy(W + static_cast<long long>(n) * p.ldw + kb + 8 * c, st + 1024 * i);
       } else if constexpr (!A_F32) {                  // activation rows, bf16
         const int a = i - NT / 8;
@@ -459,26 +493,27 @@ __global__ void reduce_rope_kernel(const float* __restrict__ P, int splits, int 
   Elem<TO>::st(o + 1, x0 * sn + x1 * c);
 }
 
-// One workgroup per sequence: sum the splits of [c ; k_R], optionally
-// RMS-normalise c ("Understanding MLA" (Dong), A2: norm on the latent only),
-// rotate k_R at the token's position, round and write the cache row.
+// One workgroup per sequence, one thread per column of the row (up to 1024):
+// sum the splits of [c ; k_R], optionally RMS-normalise c ("Understanding
+// MLA" (Dong), A2: norm on the latent only), rotate k_R at the token's
+// position, round and write the cache row. Every thread issues the loads of
+// all its splits at once, so the sums cost about one memory round trip.
 template <typename T>
-__global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ Pc, int splits_c,
-                                                     const float* __restrict__ Pr, int splits_r, int M,
-                                                     int d_c, int d_R, const T* __restrict__ gamma,
-                                                     float eps, const int32_t* __restrict__ pos,
-                                                     float theta, mla_cache cache) {
-  extern __shared__ float row[];    // d_c + d_R floats, then 4 for the reduction
+__global__ __launch_bounds__(1024) void append_kernel(const float* __restrict__ Pc, int splits_c, int ldc,
+                                                      const float* __restrict__ Pr, int splits_r, int ldr, int M,
+                                                      int d_c, int d_R, const T* __restrict__ gamma,
+                                                      float eps, const int32_t* __restrict__ pos,
+                                                      float theta, mla_cache cache) {
+  extern __shared__ float row[];    // d_c + d_R floats, then 16 for the reduction
   const int m = blockIdx.x;
   const int D = d_c + d_R;
   float* red = row + D;
   float ss = 0.f;
-  // Split sums: four independent chains so that the partial loads overlap;
-  // fixed order, hence deterministic.
-  auto split_sum = [&](const float* P, int splits, int width, int c) {
+  // Split sums: four independent chains; fixed order, hence deterministic.
+  auto split_sum = [&](const float* P, int splits, int ld, int c) {
     float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-    const long long stride = static_cast<long long>(M) * width;
-    const float* q = P + static_cast<long long>(m) * width + c;
+    const long long stride = static_cast<long long>(M) * ld;
+    const float* q = P + static_cast<long long>(m) * ld + c;
     int s = 0;
     for (; s + 4 <= splits; s += 4) {
       v0 += q[s * stride];
@@ -489,18 +524,22 @@ __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ P
     for (; s < splits; ++s) v0 += q[s * stride];
     return (v0 + v1) + (v2 + v3);
   };
-  for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
-    const float v = split_sum(Pc, splits_c, d_c, c);
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    const float v = c < d_c ? split_sum(Pc, splits_c, ldc, c) : split_sum(Pr, splits_r, ldr, c - d_c);
     row[c] = v;
-    ss += v * v;
+    if (c < d_c) ss += v * v;
   }
-  for (int c = threadIdx.x; c < d_R; c += blockDim.x) row[d_c + c] = split_sum(Pr, splits_r, d_R, c);
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  float rinv = 1.f;
+  if (gamma) {
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  }
   __syncthreads();
-  float tot = 0.f;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
-  const float rinv = gamma ? rsqrtf(tot / d_c + eps) : 1.f;
+  if (gamma) {
+    float tot = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
+    rinv = rsqrtf(tot / d_c + eps);
+  }
   const int t = pos[m];
   T* dst;
   if (cache.block_table == nullptr) {
@@ -510,17 +549,19 @@ __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ P
     dst = static_cast<T*>(cache.data) +
           (static_cast<long long>(blk) * cache.block_size + t % cache.block_size) * D;
   }
-  for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
-    float v = row[c];
-    if (gamma) v = v * rinv * Elem<T>::ld(gamma + c);
-    Elem<T>::st(dst + c, v);
-  }
-  for (int j = threadIdx.x; j < d_R / 2; j += blockDim.x) {
-    float c, s;
-    rope_cs(t, j, d_R, theta, &c, &s);
-    const float x0 = row[d_c + 2 * j], x1 = row[d_c + 2 * j + 1];
-    Elem<T>::st(dst + d_c + 2 * j, x0 * c - x1 * s);
-    Elem<T>::st(dst + d_c + 2 * j + 1, x0 * s + x1 * c);
+  for (int c = threadIdx.x; c < d_c + d_R / 2; c += blockDim.x) {
+    if (c < d_c) {
+      float v = row[c];
+      if (gamma) v = v * rinv * Elem<T>::ld(gamma + c);
+      Elem<T>::st(dst + c, v);
+    } else {
+      const int j = c - d_c;
+      float cs, sn;
+      rope_cs(t, j, d_R, theta, &cs, &sn);
+      const float x0 = row[d_c + 2 * j], x1 = row[d_c + 2 * j + 1];
+      Elem<T>::st(dst + d_c + 2 * j, x0 * cs - x1 * sn);
+      Elem<T>::st(dst + d_c + 2 * j + 1, x0 * sn + x1 * cs);
+    }
   }
 }
 
@@ -568,15 +609,21 @@ int gemm_splits(int M, int N, int K, int G, int dtype) {
   return (K + kper - 1) / kper;
 }
 
-bool gemm_direct(const GemmArgs& a) { return a.out != nullptr && a.splits == 1 && stream_ok(a); }
+bool gemm_direct(const GemmArgs& a) { return a.out != nullptr && a.splits == 1 && mfma_ok(a); }
+
+bool gemm_concat_ok(const GemmArgs& a) {
+  return stream_ok(a) && a.G == 1 && a.n_split > 0 && a.n_split % stream_nt(a.N) == 0 &&
+         (reinterpret_cast<uintptr_t>(a.W2) & 15) == 0;
+}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
+  if (a.W2 && !gemm_concat_ok(a)) return hipErrorInvalidValue;
   const int splits = a.splits;
   const int ksteps = (a.K + GBK - 1) / GBK;
   const int kper = ((ksteps + splits - 1) / splits) * GBK;
   if (stream_ok(a)) {
-    GemmP p{a.A, a.lda, a.sAg, static_cast<const uint16_t*>(a.W), a.ldw, a.sWg, a.M, a.N, a.K, kper, a.P,
-            nullptr, 0, 0, 0};
+    GemmP p{a.A, a.lda, a.sAg, static_cast<const uint16_t*>(a.W), a.ldw, a.sWg,
+            static_cast<const uint16_t*>(a.W2), a.n_split, a.M, a.N, a.K, kper, a.P, nullptr, 0, 0, 0};
     if (gemm_direct(a)) {
       p.out = a.out;
       p.ldo = a.ldo;
@@ -598,8 +645,14 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   if (mfma_ok(a)) {
-    GemmP p{a.A, a.lda, a.sAg, static_cast<const uint16_t*>(a.W), a.ldw, a.sWg, a.M, a.N, a.K, kper, a.P,
-            nullptr, 0, 0, 0};
+    GemmP p{a.A, a.lda, a.sAg, static_cast<const uint16_t*>(a.W), a.ldw, a.sWg,
+            static_cast<const uint16_t*>(a.W2), a.n_split, a.M, a.N, a.K, kper, a.P, nullptr, 0, 0, 0};
+    if (gemm_direct(a)) {
+      p.out = a.out;
+      p.ldo = a.ldo;
+      p.sOg = a.sOg;
+      p.out_bf16 = a.out_dtype == MLA_BF16;
+    }
     const int MT = a.M <= 32 ? 1 : a.M <= 64 ? 2 : 4;
     const int mblocks = (a.M + 32 * MT - 1) / (32 * MT);
     const dim3 grid((a.N + GBN - 1) / GBN, a.G, splits * mblocks);
@@ -655,16 +708,19 @@ hipError_t launch_reduce_rope(const float* P, int splits, int M, int G, int d_R,
   return hipGetLastError();
 }
 
-hipError_t launch_append(const float* Pc, int splits_c, const float* Pr, int splits_r, int M, int d_c, int d_R,
+hipError_t launch_append(const float* Pc, int splits_c, int ldc, const float* Pr, int splits_r, int ldr, int M,
+                         int d_c, int d_R,
                          const void* gamma, float eps, const int32_t* pos, float theta,
                          const mla_cache& cache, int dtype, hipStream_t stream) {
-  const size_t shmem = (static_cast<size_t>(d_c + d_R) + 8) * sizeof(float);
+  const size_t shmem = (static_cast<size_t>(d_c + d_R) + 16) * sizeof(float);
+  const int threads = std::min(1024, (d_c + d_R + 63) / 64 * 64);
   if (dtype == MLA_BF16)
-    append_kernel<uint16_t><<<M, 256, shmem, stream>>>(Pc, splits_c, Pr, splits_r, M, d_c, d_R,
-                                                       static_cast<const uint16_t*>(gamma), eps, pos, theta, cache);
+    append_kernel<uint16_t><<<M, threads, shmem, stream>>>(Pc, splits_c, ldc, Pr, splits_r, ldr, M, d_c, d_R,
+                                                           static_cast<const uint16_t*>(gamma), eps, pos, theta,
+                                                           cache);
   else
-    append_kernel<float><<<M, 256, shmem, stream>>>(Pc, splits_c, Pr, splits_r, M, d_c, d_R,
-                                                    static_cast<const float*>(gamma), eps, pos, theta, cache);
+    append_kernel<float><<<M, threads, shmem, stream>>>(Pc, splits_c, ldc, Pr, splits_r, ldr, M, d_c, d_R,
+                                                        static_cast<const float*>(gamma), eps, pos, theta, cache);
   return hipGetLastError();
 }
 

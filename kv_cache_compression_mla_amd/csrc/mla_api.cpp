@@ -141,7 +141,9 @@ size_t part_bytes(const GemmShape& s, int dtype) {
 }
 
 size_t ws_compress(const mla_dims* d, int B) {
-  return align_up(part_bytes({B, d->d_c, d->d, 1}, d->dtype)) + align_up(part_bytes({B, d->d_R, d->d, 1}, d->dtype));
+  // two products' partials, or one concatenated product's
+  return std::max(align_up(part_bytes({B, d->d_c, d->d, 1}, d->dtype)) + align_up(part_bytes({B, d->d_R, d->d, 1}, d->dtype)),
+                  align_up(part_bytes({B, d->d_c + d->d_R, d->d, 1}, d->dtype)));
 }
 
 size_t ws_absorb(const mla_dims* d, int B) {
@@ -276,14 +278,31 @@ mla_status mla_compress_append(const mla_dims* dims, int32_t B, const void* h_t,
   const int dt = dims->dtype;
   const bool f32 = dt == MLA_FP32;
   char* w = static_cast<char*>(ws);
+  const float eps = dims->norm_eps > 0.f ? dims->norm_eps : 1e-6f;
+  const int D = dims->d_c + dims->d_R;
+  // [c ; k_R] = [W_DKV ; W_KR] h_t as one product when the streaming kernel
+  // can take the two weights in one launch
+  {
+    const GemmShape s{B, D, dims->d, 1};
+    mla::GemmArgs g{h_t, dims->d, 0, f32, W_DKV, dims->d, 0, false, s.M, s.N, s.K, s.G, splits_for(s, dt),
+                    reinterpret_cast<float*>(w), dt};
+    g.W2 = W_KR;
+    g.n_split = dims->d_c;
+    if (mla::gemm_concat_ok(g)) {
+      MLA_TRY(hip_status(mla::launch_gemm(g, st), "gemm launch"));
+      const float* P = reinterpret_cast<const float*>(w);
+      return hip_status(mla::launch_append(P, g.splits, D, P + dims->d_c, g.splits, D, B, dims->d_c, dims->d_R,
+                                           gamma_kv, eps, pos, dims->rope_theta, *cache, dt, st),
+                        "append launch");
+    }
+  }
   float* Pc = reinterpret_cast<float*>(w);
   float* Pr = reinterpret_cast<float*>(w + align_up(part_bytes({B, dims->d_c, dims->d, 1}, dt)));
   const GemmShape sc{B, dims->d_c, dims->d, 1}, sr{B, dims->d_R, dims->d, 1};
   MLA_TRY(gemm(h_t, dims->d, 0, f32, W_DKV, dims->d, 0, false, sc, dt, Pc, st));
   MLA_TRY(gemm(h_t, dims->d, 0, f32, W_KR, dims->d, 0, false, sr, dt, Pr, st));
-  const float eps = dims->norm_eps > 0.f ? dims->norm_eps : 1e-6f;
-  MLA_TRY(hip_status(mla::launch_append(Pc, splits_for(sc, dt), Pr, splits_for(sr, dt), B, dims->d_c, dims->d_R,
-                                        gamma_kv, eps, pos, dims->rope_theta, *cache, dt, st),
+  MLA_TRY(hip_status(mla::launch_append(Pc, splits_for(sc, dt), dims->d_c, Pr, splits_for(sr, dt), dims->d_R, B,
+                                        dims->d_c, dims->d_R, gamma_kv, eps, pos, dims->rope_theta, *cache, dt, st),
                      "append launch"));
   return ok();
 }

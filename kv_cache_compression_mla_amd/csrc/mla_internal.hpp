@@ -72,11 +72,18 @@ struct GemmArgs {
   void* out = nullptr;
   long long ldo = 0, sOg = 0;
   int out_dtype = 0;
+  // Optional second weight (G = 1, streaming kernel only): output columns
+  // n >= n_split read W2 row n - n_split (same ldw), so two products of one
+  // activation run as one launch.
+  const void* W2 = nullptr;
+  int n_split = 0;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // True when launch_gemm stores a's product directly to a.out (one split on
 // the streaming kernel); otherwise it writes partials for an epilogue.
 bool gemm_direct(const GemmArgs& a);
+// True when launch_gemm can take a's second weight (W2, n_split).
+bool gemm_concat_ok(const GemmArgs& a);
 // Number of k splits launch_gemm would pick for a shape (used to size workspaces).
 int gemm_splits(int M, int N, int K, int G, int dtype);
 
@@ -94,7 +101,7 @@ hipError_t launch_reduce_rope(const float* P, int splits, int M, int G, int d_R,
 // Sum splits of the latent [M][d_c] and rotary key [M][d_R] partials,
 // optionally RMS-normalise the latent, rotate the key at pos[m], round, and
 // write the row to the cache at position pos[m].
-hipError_t launch_append(const float* Pc, int splits_c, const float* Pr, int splits_r, int M,
+hipError_t launch_append(const float* Pc, int splits_c, int ldc, const float* Pr, int splits_r, int ldr, int M,
                          int d_c, int d_R, const void* gamma, float eps, const int32_t* pos,
                          float theta, const mla_cache& cache, int dtype, hipStream_t stream);
 

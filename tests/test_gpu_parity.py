@@ -263,6 +263,39 @@ def test_attention_alone_against_oracle():
         check_attention(inp, st, q, f"attn s={splits}")
 
 
+def test_empty_sequences_in_a_batch():
+    """Sequences of length 0 among others (each gets one empty chunk in the
+    device plan): zeros and lse = -inf for them, the oracle for the rest, with
+    the balanced plan and with explicit splits."""
+    cfg = V3.with_(name="v3_empty", B=4, ctx=(300, 5, 1000, 64), seed=22)
+    inp = make_inputs(cfg)
+    q = gen.make_query(cfg)
+    fill_append_slots(inp)
+    lens = np.array([0, 6, 0, 65], dtype=np.int32)
+    from kv_cache_compression_mla_amd.step import to_device
+    for splits in (0, 1, 3):
+        st = DeviceStep(inp, num_splits=splits)
+        st.seq_lens.copy_(torch.from_numpy(lens).to(st.seq_lens.device))
+        st.o_lat.fill_(float("nan"))
+        mla.mla_decode_attn(st.dims, to_device(q, cfg.dtype), st.cdesc, st.seq_lens, int(lens.max()),
+                            st.o_lat, st.lse, st.ws, splits)
+        torch.cuda.synchronize()
+        o_lat, lse = st.host(st.o_lat), st.host(st.lse)
+        q64 = gen.to_f64(q, cfg.dtype)
+        for b in range(cfg.B):
+            n = int(lens[b])
+            if n == 0:
+                assert np.array_equal(o_lat[b], np.zeros_like(o_lat[b])), (splits, b)
+                assert np.all(np.isneginf(lse[b])), (splits, b)
+                continue
+            rows = gen.to_f64(inp.rows(b, n), cfg.dtype)
+            ref_o, ref_l = om.attend_absorbed(q64[b, :, :cfg.d_c], q64[b, :, cfg.d_c:], rows, cfg.scale)
+            e_o = rel_err(o_lat[b], ref_o)
+            e_l = np.abs(lse[b] - ref_l).max() / max(np.abs(ref_l).max(), 1.0)
+            say(f"empty-mix s={splits} b={b} L={n} o_lat {e_o:.2e} lse {e_l:.2e}")
+            assert e_o <= tol(cfg) and e_l <= tol(cfg), (splits, b, e_o, e_l)
+
+
 @pytest.mark.parametrize("name,seqs,unabs", [
     ("v3_b1_ctx4k", [0], True),
     ("v3_b64_ctx8k", [0, 63], False),
