@@ -87,6 +87,8 @@ CONFIGS = {
     "v3_b128_ragged_paged": MLAConfig(name="v3_b128_ragged_paged", B=128,
                                       ctx_range=(1024, 16384), paged=True,
                                       block_size=64, **_V3),
+    # the RMS-normalised latent variant at the headline size
+    "v3_b64_ctx8k_norm": MLAConfig(name="v3_b64_ctx8k_norm", B=64, ctx=(8192,) * 64, gamma=True, **_V3),
 }
 CONFIG_ORDER = list(CONFIGS)
 
@@ -128,6 +130,13 @@ def _draw(rng, shape, std, dtype, chunk=1 << 24):
             v *= np.float32(std)
         out[s:e] = f32_to_bf16_bits(v) if dtype == "bf16" else v
     return out.reshape(shape)
+
+
+def _draw_cols(rng, shape, col_std, dtype):
+    """N(0, col_std[j]^2) in column j of rows of shape [n][len(col_std)],
+    rounded once to the storage dtype."""
+    v = rng.standard_normal(shape, dtype=np.float32) * np.asarray(col_std, dtype=np.float32)
+    return f32_to_bf16_bits(v) if dtype == "bf16" else v
 
 
 def _nan_fill(shape, dtype):
@@ -212,13 +221,25 @@ def make_inputs(cfg: MLAConfig, with_weights: bool = True) -> MLAInputs:
     weights = make_weights(cfg) if with_weights else {}
     h_t = _draw(r["h_t"], (cfg.B, cfg.d), 1.0, dt)
     hist = r["history"]
+    if cfg.gamma:
+        # latents stored by the normalised variant have unit RMS before the
+        # gain: column j of the latent part ~ N(0, gamma_j^2); the rotary
+        # part is not normalised
+        g = to_f64(make_weights(cfg)["gamma_kv"], dt) if not with_weights else to_f64(weights["gamma_kv"], dt)
+        col_std = np.concatenate([np.abs(g), np.full(cfg.d_R, hist_std)])
+
+        def draw_hist(n):
+            return _draw_cols(hist, (n, D), col_std, dt)
+    else:
+        def draw_hist(n):
+            return _draw(hist, (n, D), hist_std, dt)
     if not cfg.paged:
         cap = int(seq_lens.max()) + cfg.cap_pad
         cache = _nan_fill((cfg.B, cap, D), dt)
         for b in range(cfg.B):
             n = int(ctx[b])
             if n:
-                cache[b, :n] = _draw(hist, (n, D), hist_std, dt)
+                cache[b, :n] = draw_hist(n)
         return MLAInputs(cfg, weights, h_t, ctx, seq_lens, cache, None, cap)
     bs = cfg.block_size
     nblk = (seq_lens + bs - 1) // bs
@@ -234,7 +255,7 @@ def make_inputs(cfg: MLAConfig, with_weights: bool = True) -> MLAInputs:
         off += nb
         n = int(ctx[b])
         if n:
-            rows = _draw(hist, (n, D), hist_std, dt)
+            rows = draw_hist(n)
             full = n // bs
             if full:
                 pool[table[b, :full]] = rows[:full * bs].reshape(full, bs, D)

@@ -301,6 +301,7 @@ def test_empty_sequences_in_a_batch():
     ("v3_b64_ctx8k", [0, 63], False),
     ("v3_b8_ctx32k", [3], False),
     ("v3_b128_ragged_paged", None, False),
+    ("v3_b64_ctx8k_norm", [5], False),
 ])
 def test_full_size_configs_sampled(name, seqs, unabs):
     """The configured workloads at full size, in the launch configuration the

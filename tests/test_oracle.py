@@ -334,3 +334,19 @@ def test_generator_layout_and_poison():
     assert gen.context_lengths(c).tolist() == [8192] * 64
     r = gen.context_lengths(gen.CONFIGS["v3_b128_ragged_paged"])
     assert r.min() >= 1024 and r.max() <= 16384 and r.size == 128
+
+
+def test_generator_history_of_the_normalised_variant():
+    """With the latent norm, stored latents have unit RMS before the gain:
+    column j of the history's latent part has spread |gamma_j|; the rotary
+    part keeps the unnormalised spread."""
+    cfg = gen.CONFIGS["v3_b1_ctx4k"].with_(name="hist_norm", ctx=(4000,), gamma=True, seed=3)
+    inp = gen.make_inputs(cfg, with_weights=False)
+    g = np.abs(gen.to_f64(gen.make_weights(cfg)["gamma_kv"], "bf16"))
+    rows = gen.to_f64(inp.rows(0, 4000), "bf16")
+    std = rows.std(axis=0)
+    np.testing.assert_allclose(std[:cfg.d_c], g, rtol=0.08)
+    np.testing.assert_allclose(std[cfg.d_c:], cfg.w_std * np.sqrt(cfg.d), rtol=0.08)
+    # the stored latent rows then have RMS close to that of gamma
+    rms = np.sqrt(np.mean(rows[:, :cfg.d_c] ** 2, axis=1))
+    assert abs(np.median(rms) - np.sqrt(np.mean(g ** 2))) < 0.05
