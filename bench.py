@@ -35,7 +35,8 @@ def log(msg):
 
 
 def attn_work(cfg, seq_lens):
-    """Algorithmic bytes and FLOPs of one mla_decode_attn call."""
+    """Algorithmic bytes and FLOPs of one attention call (seq_lens: rows
+    attended per sequence; the entry counts for sparse attention)."""
     rows = int(seq_lens.sum())
     row_bytes = cfg.D * 2
     cache_bytes = rows * row_bytes
@@ -63,9 +64,10 @@ def traffic_from_profile(workload):
         return None
 
 
-def cpu_baseline(inp, budget_s):
+def cpu_baseline(inp, budget_s, topk=None):
     """Time the float64 oracle (unabsorbed: per-head K and V rebuilt from every
-    cached latent) on whole sequences of the workload until the budget is used."""
+    attended latent) on whole sequences of the workload until the budget is
+    used. topk: (indices, counts) for sparse attention."""
     import numpy as np
     from kv_cache_compression_mla_amd import inputs as gen
     from oracle import mla_oracle as om
@@ -76,10 +78,11 @@ def cpu_baseline(inp, budget_s):
     for b in range(cfg.B):
         h = gen.to_f64(inp.h_t[b], cfg.dtype)
         prior = gen.to_f64(inp.rows(b, int(inp.ctx[b])), cfg.dtype)
+        idx = None if topk is None else topk[0][b, :int(topk[1][b])]
         t0 = time.perf_counter()
-        om.decode_step(h, prior, W, int(inp.ctx[b]), cfg.theta, cfg.scale, cfg.dtype)
+        om.decode_step(h, prior, W, int(inp.ctx[b]), cfg.theta, cfg.scale, cfg.dtype, idx=idx)
         t_used += time.perf_counter() - t0
-        done_rows += int(inp.seq_lens[b])
+        done_rows += int(inp.seq_lens[b]) if topk is None else int(topk[1][b])
         nseq += 1
         if t_used >= budget_s:
             break
@@ -120,7 +123,8 @@ def main():
     inp = gen.make_inputs(cfg)
     log(f"inputs for {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
     st = DeviceStep(inp, num_splits=args.num_splits)
-    rows, cache_bytes, attn_bytes, attn_flops = attn_work(cfg, inp.seq_lens)
+    attended = st.topk_counts_host if cfg.topk else inp.seq_lens
+    rows, cache_bytes, attn_bytes, attn_flops = attn_work(cfg, attended)
     splits = st.splits
     log(f"B={cfg.B} rows={rows} splits={splits} kernel={mla.decode_kernel(st.dims)}")
 
@@ -163,7 +167,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "ctx": int(inp.ctx.max()),
                    "rows_attended": rows, "heads": cfg.H, "d_c": cfg.d_c, "d_R": cfg.d_R,
-                   "paged": cfg.paged, "num_splits": splits},
+                   "paged": cfg.paged, "num_splits": splits, "topk": cfg.topk},
         "attn_ms": round(attn_ms, 5),
         "cache_GBps": round(cache_gbps, 1),
         "pct_hbm_roofline": round(100 * achieved_gbps / HBM_PEAK_GBPS, 2),
@@ -175,7 +179,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(
+            inp, args.cpu_seconds, (st.topk_idx_host, st.topk_counts_host) if cfg.topk else None)
     print(json.dumps(result), flush=True)
 
 

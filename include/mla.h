@@ -170,6 +170,36 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q,
                            void* stream);
 
 /*
+ * mla_decode_attn_sparse -- every head attends against a given subset of the
+ * latent cache: sequence b attends only to the counts[b] rows listed in
+ * indices[b][0..counts[b]) (positions in its cache), the top-k pattern of a
+ * sparse selector layered above MLA ([KB] section 4, "Scaling to V3.2 +
+ * sparse attention": a top-K subset of the cached latents, k = 2048, per
+ * query, each candidate a single d_c + d_R row). For head i:
+ *   s(i,j)   = scale * (q(b,i) . row(b, indices[b][j]))   j < counts[b]
+ *   o_lat(i) = sum_j softmax_j(s(i,j)) * row(b, indices[b][j])[0:d_c]
+ *   lse(i)   = ln sum_j exp(s(i,j))
+ * Each listed entry is one term of the softmax (a repeated index counts
+ * once per listing); the order of the list does not matter.
+ *   indices  [B][topk] int32 device; entries past counts[b] are not read.
+ *            Device-side precondition: every listed position is a row of
+ *            sequence b's cache (contiguous: < capacity; paged: its block
+ *            table entry is valid).
+ *   topk     row stride of indices (> 0), and the host bound of counts
+ *   counts   [B] int32 device, 0 <= counts[b] <= topk; 0 gives an all-zero
+ *            o_lat row and lse = -inf
+ *   num_splits, o_lat, lse, ws: as for mla_decode_attn with max_seq_len =
+ *            topk (the workspace of mla_workspace_bytes(dims, B, topk,
+ *            num_splits) suffices)
+ * Errors: as for mla_decode_attn; MLA_ERR_SHAPE if topk <= 0, MLA_ERR_NULL
+ * if indices or counts is NULL, MLA_ERR_ALIGN unless both are 4-byte aligned.
+ */
+mla_status mla_decode_attn_sparse(const mla_dims* dims, int32_t B, const void* q,
+                                  const mla_cache* cache, const int32_t* indices, int32_t topk,
+                                  const int32_t* counts, int32_t num_splits, float* o_lat,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * mla_out_proj -- back to the hidden width.
  *   o_heads(b,i) = W_UV(i) o_lat(b,i)       ([CASS] value projection after the
  *                                            weighted sum)

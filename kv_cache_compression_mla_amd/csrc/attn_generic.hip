@@ -16,9 +16,13 @@ namespace {
 constexpr int GT = 256;          // threads per workgroup
 constexpr int MAX_DC_PER_T = 4;  // d_c <= 1024
 
+// Row of entry u of sequence b: position u, or the listed position
+// indices[b][u] for sparse attention.
 template <typename T>
 __device__ __forceinline__ const T* g_row_ptr(const T* cache, const int32_t* table, long long cap,
-                                              int bs, int maxb, int D, int b, int u) {
+                                              int bs, int maxb, int D, int b, int u, const int32_t* indices,
+                                              int topk) {
+  if (indices) u = indices[static_cast<long long>(b) * topk + u];
   if (table == nullptr) return cache + (b * cap + u) * static_cast<long long>(D);
   const int blk = table[b * maxb + u / bs];
   return cache + (static_cast<long long>(blk) * bs + u % bs) * D;
@@ -73,7 +77,8 @@ __global__ __launch_bounds__(GT) void attn_generic_kernel(AttnArgs a) {
     const int u = base + tid;
     float sc = -INFINITY;
     if (u < r1) {
-      const T* row = g_row_ptr(cache, a.block_table, a.capacity, a.block_size, a.max_blocks, D, b, u);
+      const T* row = g_row_ptr(cache, a.block_table, a.capacity, a.block_size, a.max_blocks, D, b, u, a.indices,
+                               a.topk);
       float dot = 0.f;
       for (int k = 0; k < D; ++k) dot += qs[k] * Elem<T>::ld(row + k);
       sc = dot * sl2;
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(GT) void attn_generic_kernel(AttnArgs a) {
         float x = acc[j] * alpha;
         for (int t = 0; t < nrow; ++t) {
           const T* row = g_row_ptr(cache, a.block_table, a.capacity, a.block_size, a.max_blocks, D, b,
-                                   base + t);
+                                   base + t, a.indices, a.topk);
           x += ps[t] * Elem<T>::ld(row + c);
         }
         acc[j] = x;

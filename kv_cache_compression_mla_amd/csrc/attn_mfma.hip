@@ -94,6 +94,10 @@ constexpr int SMEM_BYTES = FLAG_OFF + 16;         // 162832 (of 163840)
 constexpr int CONTIG = 0;        // [B][capacity][576]
 constexpr int PAGED8 = 1;        // paged, block_size >= 8: 8-row groups share a block
 constexpr int PAGED_SMALL = 2;   // paged, block_size < 8
+constexpr int GATHER_CONTIG = 3; // listed rows (sparse attention) of a contiguous cache
+constexpr int GATHER_PAGED = 4;  // listed rows of a paged cache
+// modes whose 8-row groups are not one contiguous run: one pointer per row
+__host__ __device__ constexpr bool per_row(int pm) { return pm == PAGED_SMALL || pm >= GATHER_CONTIG; }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -117,6 +121,8 @@ struct Params {
   float* part_o;          // [grid][H][512] partials, by chunk
   float* part_ml;         // [grid][H][2]
   int2* plan_seq;         // [B]: (first chunk, chunks) of each sequence
+  const int32_t* indices; // gather modes: [B][topk] listed rows (seq_lens = counts)
+  int topk;
 };
 
 // ---- chunk plan ----
@@ -280,7 +286,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 template <int PM>
 __device__ __forceinline__ const uint16_t* row_ptr(const Params& p, int b, int u) {
-  if constexpr (PM == CONTIG) {
+  if constexpr (PM == GATHER_CONTIG || PM == GATHER_PAGED) {
+    const const_i32* ix = (const const_i32*)(p.indices);   // listed position of entry u
+    u = ix[static_cast<long long>(b) * p.topk + u];
+  }
+  if constexpr (PM == CONTIG || PM == GATHER_CONTIG) {
     return p.cache + b * p.seq_stride + static_cast<long long>(u) * DW;
   } else {
     const const_i32* tab = (const const_i32*)(p.table);
@@ -331,7 +341,7 @@ __device__ __forceinline__ TileCopy plan_copy(const Params& p, int b, int r0, in
   const int last = row_end - 1;
   const int j = lane >> 3;
   const int chunk = (lane & 7) ^ rope_sw(8 * w + j);
-  if constexpr (PM == PAGED_SMALL) {
+  if constexpr (per_row(PM)) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) c.row[k] = row_ptr<PM>(p, b, min(first + k, last));
     const uint16_t* mine = c.row[0];
@@ -359,7 +369,7 @@ __device__ __forceinline__ void copy_part(const TileCopy& c, int k, uint32_t lat
                                           uint32_t lane_off) {
   if (k < 8) {
     copy_s(c.row[k], lane_off, lat + (8 * w + k) * LROW);
-  } else if constexpr (PM == PAGED_SMALL) {
+  } else if constexpr (per_row(PM)) {
     copy_v(c.rope_ptr, rope + w * 1024);
   } else {
     copy_s(c.rope_base, c.rope_voff, rope + w * 1024);
@@ -845,12 +855,17 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
   p.part_o = a.part_o;
   p.part_ml = a.part_ml;
   p.plan_seq = a.plan_seq;
+  p.indices = a.indices;
+  p.topk = a.topk;
   const dim3 grid(a.grid);
-  const int pm = !a.block_table ? CONTIG : (a.block_size >= 8 ? PAGED8 : PAGED_SMALL);
-#define MLA_ATTN_LAUNCH(NW)                                                               \
-  if (pm == CONTIG) attn_mfma_kernel<NW, CONTIG><<<grid, NTHREADS, 0, stream>>>(p);       \
-  else if (pm == PAGED8) attn_mfma_kernel<NW, PAGED8><<<grid, NTHREADS, 0, stream>>>(p);  \
-  else attn_mfma_kernel<NW, PAGED_SMALL><<<grid, NTHREADS, 0, stream>>>(p);
+  const int pm = a.indices ? (a.block_table ? GATHER_PAGED : GATHER_CONTIG)
+                           : (!a.block_table ? CONTIG : (a.block_size >= 8 ? PAGED8 : PAGED_SMALL));
+#define MLA_ATTN_LAUNCH(NW)                                                                       \
+  if (pm == CONTIG) attn_mfma_kernel<NW, CONTIG><<<grid, NTHREADS, 0, stream>>>(p);               \
+  else if (pm == PAGED8) attn_mfma_kernel<NW, PAGED8><<<grid, NTHREADS, 0, stream>>>(p);          \
+  else if (pm == PAGED_SMALL) attn_mfma_kernel<NW, PAGED_SMALL><<<grid, NTHREADS, 0, stream>>>(p); \
+  else if (pm == GATHER_CONTIG) attn_mfma_kernel<NW, GATHER_CONTIG><<<grid, NTHREADS, 0, stream>>>(p); \
+  else attn_mfma_kernel<NW, GATHER_PAGED><<<grid, NTHREADS, 0, stream>>>(p);
   switch (a.H / 32) {
     case 1: MLA_ATTN_LAUNCH(1) break;
     case 2: MLA_ATTN_LAUNCH(2) break;

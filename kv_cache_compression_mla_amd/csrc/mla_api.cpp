@@ -363,17 +363,25 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const 
   return ok();
 }
 
-mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
-                           const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_lat,
-                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Dense attention (indices NULL: entry u of sequence b is row u, seq_lens
+// rows) or sparse attention (entry u is row indices[b*topk + u], seq_lens
+// holds the entry counts, max_seq_len = topk).
+mla_status decode_attn_impl(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
+                            const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_lat,
+                            float* lse, void* ws, size_t ws_bytes, void* stream, const int32_t* indices,
+                            int32_t topk) {
   MLA_TRY(check_dims(dims));
   if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
   if (max_seq_len < 0 || num_splits < 0) return fail(MLA_ERR_SHAPE, "negative max_seq_len or num_splits");
   if (!q || !seq_lens || !o_lat) return fail(MLA_ERR_NULL, "decode_attn: NULL pointer");
   MLA_TRY(check_cache(dims, cache));
-  if (!cache->block_table && max_seq_len > cache->capacity)
+  if (!indices && !cache->block_table && max_seq_len > cache->capacity)
     return fail(MLA_ERR_SHAPE, "max_seq_len %d exceeds capacity %d", max_seq_len, cache->capacity);
-  if (cache->block_table &&
+  if (!indices && cache->block_table &&
       static_cast<long long>(max_seq_len) > static_cast<long long>(cache->max_blocks) * cache->block_size)
     return fail(MLA_ERR_SHAPE, "max_seq_len exceeds max_blocks * block_size");
   for (const void* p : {q, static_cast<const void*>(seq_lens), static_cast<const void*>(o_lat)})
@@ -406,6 +414,8 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const
   a.o_lat = o_lat;
   a.lse = lse;
   a.dtype = dims->dtype;
+  a.indices = indices;
+  a.topk = topk;
   if (mfma) {
     // the device plans the chunks (balanced when num_splits is 0) and merges them
     const int s = mfma_splits(num_splits, max_seq_len);
@@ -434,6 +444,28 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const
   MLA_TRY(hip_status(mla::launch_attn_generic(a, st), "attention launch"));
   if (a.splits > 1) MLA_TRY(hip_status(mla::launch_attn_combine(a, st), "combine launch"));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
+                           const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_lat,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return decode_attn_impl(dims, B, q, cache, seq_lens, max_seq_len, num_splits, o_lat, lse, ws, ws_bytes, stream,
+                          nullptr, 0);
+}
+
+mla_status mla_decode_attn_sparse(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
+                                  const int32_t* indices, int32_t topk, const int32_t* counts, int32_t num_splits,
+                                  float* o_lat, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (topk <= 0) return fail(MLA_ERR_SHAPE, "decode_attn_sparse: topk must be positive");
+  if (!indices || !counts) return fail(MLA_ERR_NULL, "decode_attn_sparse: NULL indices or counts");
+  if ((reinterpret_cast<uintptr_t>(indices) | reinterpret_cast<uintptr_t>(counts)) & 3)
+    return fail(MLA_ERR_ALIGN, "decode_attn_sparse: indices and counts must be 4-byte aligned");
+  return decode_attn_impl(dims, B, q, cache, counts, topk, num_splits, o_lat, lse, ws, ws_bytes, stream, indices,
+                          topk);
 }
 
 mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat, const void* W_UV, const void* W_O,

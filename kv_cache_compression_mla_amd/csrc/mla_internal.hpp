@@ -125,6 +125,10 @@ struct AttnArgs {
   // of the plan it computes on the device (splits = 0: balanced plan)
   int grid = 0;
   int2* plan_seq = nullptr;
+  // sparse attention: entry u of sequence b is the row at indices[b*topk + u]
+  // (seq_lens then holds the entry counts)
+  const int32_t* indices = nullptr;
+  int topk = 0;
 };
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream);

@@ -33,7 +33,7 @@ BF16_NAN = np.uint16(0x7FC0)
 # Order in which child random streams are spawned from the seed. Fixed so that
 # every consumer draws identical values.
 _STREAMS = ("W_DKV", "W_KR", "W_DQ", "W_UQ", "W_QR", "W_UK", "W_UV", "W_O",
-            "h_t", "history", "ctx", "pages", "gamma", "q")
+            "h_t", "history", "ctx", "pages", "gamma", "q", "topk")
 
 
 @dataclass(frozen=True)
@@ -57,6 +57,7 @@ class MLAConfig:
     w_std: float = 0.02
     softmax_scale: float = 0.0            # 0 -> 1/sqrt(d_h + d_R)
     gamma: bool = False                   # draw an RMSNorm weight for the latent
+    topk: int = 0                         # > 0: attention over a listed top-k subset of rows
     seed: int = 0
 
     @property
@@ -89,6 +90,8 @@ CONFIGS = {
                                       block_size=64, **_V3),
     # the RMS-normalised latent variant at the headline size
     "v3_b64_ctx8k_norm": MLAConfig(name="v3_b64_ctx8k_norm", B=64, ctx=(8192,) * 64, gamma=True, **_V3),
+    # sparse attention over a top-2048 list per sequence at the headline size
+    "v3_b64_ctx8k_topk2048": MLAConfig(name="v3_b64_ctx8k_topk2048", B=64, ctx=(8192,) * 64, topk=2048, **_V3),
 }
 CONFIG_ORDER = list(CONFIGS)
 
@@ -263,6 +266,21 @@ def make_inputs(cfg: MLAConfig, with_weights: bool = True) -> MLAInputs:
             if rem:
                 pool[table[b, full], :rem] = rows[full * bs:]
     return MLAInputs(cfg, weights, h_t, ctx, seq_lens, pool, table, 0)
+
+
+def make_topk_indices(cfg: MLAConfig, seq_lens: np.ndarray, topk: int):
+    """A seeded top-k list per sequence, as a selector above the cache would
+    hand it over: (indices [B][topk] int32, counts [B] int32). Sequence b
+    lists min(topk, L_b) distinct positions of [0, L_b) in random order (the
+    appended row among the candidates); unused entries are -1."""
+    rng = _rngs(cfg.seed)["topk"]
+    B = len(seq_lens)
+    idx = np.full((B, topk), -1, dtype=np.int32)
+    counts = np.minimum(np.asarray(seq_lens, dtype=np.int64), topk).astype(np.int32)
+    for b in range(B):
+        n = int(counts[b])
+        idx[b, :n] = rng.choice(int(seq_lens[b]), size=n, replace=False).astype(np.int32)
+    return idx, counts
 
 
 def make_query(cfg: MLAConfig, q_std: float = 0.5) -> np.ndarray:

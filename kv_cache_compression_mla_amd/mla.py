@@ -48,6 +48,10 @@ _SIGS = {
                                        ctypes.POINTER(MLACache), ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_decode_attn_sparse": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.POINTER(MLACache), ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_out_proj": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32] + [ctypes.c_void_p] * 6
                      + [ctypes.c_size_t, ctypes.c_void_p]),
     "mla_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
@@ -165,6 +169,19 @@ def mla_decode_attn(dims, q, cache: MLACache, seq_lens, max_seq_len: int, o_lat,
         ctypes.byref(dims), B, _ptr(q, dt, "q"), ctypes.byref(cache), _ptr(seq_lens, torch.int32, "seq_lens"),
         int(max_seq_len), int(num_splits), _ptr(o_lat, torch.float32, "o_lat"),
         _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"), wsz, _stream(stream)), "mla_decode_attn")
+
+
+def mla_decode_attn_sparse(dims, q, cache: MLACache, indices, counts, o_lat, lse=None, ws=None,
+                           num_splits: int = 0, stream=None):
+    """indices [B][topk] int32, counts [B] int32 (entries used per sequence)."""
+    dt = dims.torch_dtype
+    B = q.shape[0]
+    topk = int(indices.shape[1])
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().mla_decode_attn_sparse(
+        ctypes.byref(dims), B, _ptr(q, dt, "q"), ctypes.byref(cache), _ptr(indices, torch.int32, "indices"),
+        topk, _ptr(counts, torch.int32, "counts"), int(num_splits), _ptr(o_lat, torch.float32, "o_lat"),
+        _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"), wsz, _stream(stream)), "mla_decode_attn_sparse")
 
 
 def mla_out_proj(dims, o_lat, W_UV, W_O, o_heads, out, ws, stream=None):

@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from . import mla
-from .inputs import MLAInputs
+from .inputs import MLAInputs, make_topk_indices as gen_topk
 
 
 def to_device(a: Optional[np.ndarray], dtype: str, device="cuda") -> Optional[torch.Tensor]:
@@ -46,7 +46,13 @@ class DeviceStep:
         self.cdesc = mla.make_cache(self.cache, self.block_table)
         B, H, D = cfg.B, cfg.H, cfg.D
         tdt = self.dims.torch_dtype
-        ws_bytes = max(mla.workspace_bytes(self.dims, B, self.max_seq_len, s)
+        if cfg.topk:
+            # sparse attention over a seeded top-k list per sequence
+            idx, counts = gen_topk(cfg, inp.seq_lens, cfg.topk)
+            self.topk_idx_host, self.topk_counts_host = idx, counts
+            self.topk_idx = torch.from_numpy(idx).to(device)
+            self.topk_counts = torch.from_numpy(counts).to(device)
+        ws_bytes = max(mla.workspace_bytes(self.dims, B, max(self.max_seq_len, cfg.topk), s)
                        for s in (num_splits, *ws_splits))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         self.q = torch.empty(B, H, D, dtype=tdt, device=device)
@@ -57,7 +63,8 @@ class DeviceStep:
 
     @property
     def splits(self) -> int:
-        return mla.decode_num_splits(self.dims, self.cfg.B, self.max_seq_len, self.num_splits)
+        n = self.cfg.topk if self.cfg.topk else self.max_seq_len
+        return mla.decode_num_splits(self.dims, self.cfg.B, n, self.num_splits)
 
     def compress_append(self):
         mla.mla_compress_append(self.dims, self.h_t, self.W["W_DKV"], self.W["W_KR"],
@@ -68,9 +75,13 @@ class DeviceStep:
                          self.W["W_UK"], self.pos, self.q, self.ws)
 
     def decode_attn(self, num_splits: Optional[int] = None):
-        mla.mla_decode_attn(self.dims, self.q, self.cdesc, self.seq_lens, self.max_seq_len,
-                            self.o_lat, self.lse, self.ws,
-                            self.num_splits if num_splits is None else num_splits)
+        s = self.num_splits if num_splits is None else num_splits
+        if self.cfg.topk:
+            mla.mla_decode_attn_sparse(self.dims, self.q, self.cdesc, self.topk_idx, self.topk_counts,
+                                       self.o_lat, self.lse, self.ws, s)
+        else:
+            mla.mla_decode_attn(self.dims, self.q, self.cdesc, self.seq_lens, self.max_seq_len,
+                                self.o_lat, self.lse, self.ws, s)
 
     def out_proj(self):
         mla.mla_out_proj(self.dims, self.o_lat, self.W["W_UV"], self.W["W_O"], self.o_heads,

@@ -206,6 +206,19 @@ def attend_absorbed(q_lat, qR, rows, scale: float):
     return o_lat, m + np.log(l)
 
 
+def attend_sparse(q_lat, qR, rows, idx, scale: float):
+    """Attention restricted to listed rows: the softmax runs over the entries
+    idx[0..n) of a top-K list, each naming one stored row ([KB] section 4,
+    "Scaling to V3.2 + sparse attention": a top-K subset of the cached
+    latents per query). Every entry is one term; an empty list gives zeros
+    and lse = -inf."""
+    idx = np.asarray(idx, dtype=np.int64)
+    H, d_c = q_lat.shape
+    if idx.size == 0:
+        return np.zeros((H, d_c)), np.full(H, -np.inf)
+    return attend_absorbed(q_lat, qR, np.asarray(rows, dtype=np.float64)[idx], scale)
+
+
 def expand_out(o_lat, W_UV) -> np.ndarray:
     """o(i) = W_UV(i) o_lat(i): the value up-projection applied after the
     weighted sum ([CASS] "End-to-end flow"; [TIW])."""
@@ -218,30 +231,37 @@ def expand_out(o_lat, W_UV) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def decode_step(h, prior_rows, W, pos: int, theta: float, scale: float,
-                dtype: str, gamma=None, eps: float = 1e-6) -> dict:
+                dtype: str, gamma=None, eps: float = 1e-6, idx=None) -> dict:
     """One decode step of one sequence, unabsorbed (the definition).
 
     prior_rows: [pos][D] stored rows 0..pos-1 (float64 of the stored values).
     W: dict of float64 weights (W_DKV, W_KR, W_DQ or None, W_UQ, W_QR, W_UK,
-    W_UV, W_O). Returns the stored new row, per-head outputs o and out.
+    W_UV, W_O). idx: None (attend to every row, the new one included) or a
+    top-K list of positions to attend to ([KB] section 4). Returns the
+    stored new row, per-head outputs o and out.
     """
     new = store_round(compress_row(h, W["W_DKV"], W["W_KR"], pos, theta, gamma, eps), dtype)
     rows = np.concatenate([np.asarray(prior_rows, dtype=np.float64).reshape(-1, new.size),
                            new[None, :]], axis=0)
+    if idx is not None:
+        rows = rows[np.asarray(idx, dtype=np.int64)]
     qC, qR = query(h, W["W_DQ"], W["W_UQ"], W["W_QR"], pos, theta)
     o = attend_unabsorbed(qC, qR, rows, W["W_UK"], W["W_UV"], scale)
     return {"row": new, "qC": qC, "qR": qR, "o": o, "out": out_proj(o, W["W_O"])}
 
 
 def decode_step_absorbed(h, prior_rows, W, pos: int, theta: float, scale: float,
-                         dtype: str, gamma=None, eps: float = 1e-6) -> dict:
+                         dtype: str, gamma=None, eps: float = 1e-6, idx=None) -> dict:
     """Same step in the absorbed form; also returns q = [q_lat ; q_R], o_lat, lse."""
     new = store_round(compress_row(h, W["W_DKV"], W["W_KR"], pos, theta, gamma, eps), dtype)
     rows = np.concatenate([np.asarray(prior_rows, dtype=np.float64).reshape(-1, new.size),
                            new[None, :]], axis=0)
     qC, qR = query(h, W["W_DQ"], W["W_UQ"], W["W_QR"], pos, theta)
     q_lat = absorb_q(qC, W["W_UK"])
-    o_lat, lse = attend_absorbed(q_lat, qR, rows, scale)
+    if idx is None:
+        o_lat, lse = attend_absorbed(q_lat, qR, rows, scale)
+    else:
+        o_lat, lse = attend_sparse(q_lat, qR, rows, idx, scale)
     o = expand_out(o_lat, W["W_UV"])
     return {"row": new, "q": np.concatenate([q_lat, qR], axis=1), "o_lat": o_lat,
             "lse": lse, "o": o, "out": out_proj(o, W["W_O"])}

@@ -53,11 +53,15 @@ def oracle_seq(inp, W, b, absorbed=True, unabsorbed=True):
     prior = gen.to_f64(inp.rows(b, int(inp.ctx[b])), cfg.dtype)
     pos = int(inp.ctx[b])
     g = W["gamma_kv"]
+    idx = None
+    if cfg.topk:
+        lists, counts = gen.make_topk_indices(cfg, inp.seq_lens, cfg.topk)
+        idx = lists[b, :int(counts[b])]
     res = {}
     if absorbed:
-        res["abs"] = om.decode_step_absorbed(h, prior, W, pos, cfg.theta, cfg.scale, cfg.dtype, g)
+        res["abs"] = om.decode_step_absorbed(h, prior, W, pos, cfg.theta, cfg.scale, cfg.dtype, g, idx=idx)
     if unabsorbed:
-        res["unabs"] = om.decode_step(h, prior, W, pos, cfg.theta, cfg.scale, cfg.dtype, g)
+        res["unabs"] = om.decode_step(h, prior, W, pos, cfg.theta, cfg.scale, cfg.dtype, g, idx=idx)
     return res
 
 
@@ -296,12 +300,75 @@ def test_empty_sequences_in_a_batch():
             assert e_o <= tol(cfg) and e_l <= tol(cfg), (splits, b, e_o, e_l)
 
 
+def sparse_only(inp, q_bits, lists, counts, num_splits):
+    """Run mla_decode_attn_sparse alone on a generator-made query."""
+    st = DeviceStep(inp, num_splits=num_splits)
+    from kv_cache_compression_mla_amd.step import to_device
+    dev = st.seq_lens.device
+    mla.mla_decode_attn_sparse(st.dims, to_device(q_bits, inp.cfg.dtype), st.cdesc,
+                               torch.from_numpy(lists).to(dev), torch.from_numpy(counts).to(dev),
+                               st.o_lat, st.lse, st.ws, num_splits)
+    torch.cuda.synchronize()
+    return st
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_sparse_attention_against_oracle(paged):
+    """Attention over seeded top-k lists (random order, some shorter than k,
+    one empty, one of a single entry) against the oracle, with the balanced
+    plan and explicit splits."""
+    cfg = V3.with_(name="v3_sparse", B=5, ctx=(300, 1000, 64, 2500, 900), seed=23, paged=paged, block_size=64)
+    inp = make_inputs(cfg)
+    q = gen.make_query(cfg)
+    fill_append_slots(inp)
+    lists, counts = gen.make_topk_indices(cfg, inp.seq_lens, 256)
+    counts[4] = 0                      # empty list
+    counts[2] = 1                      # a single entry
+    q64 = gen.to_f64(q, cfg.dtype)
+    for splits in (0, 1, 3):
+        st = sparse_only(inp, q, lists, counts, splits)
+        o_lat, lse = st.host(st.o_lat), st.host(st.lse)
+        for b in range(cfg.B):
+            n = int(counts[b])
+            if n == 0:
+                assert not o_lat[b].any() and np.all(np.isneginf(lse[b])), (splits, b)
+                continue
+            rows = gen.to_f64(inp.rows(b, int(inp.seq_lens[b])), cfg.dtype)
+            ref_o, ref_l = om.attend_sparse(q64[b, :, :cfg.d_c], q64[b, :, cfg.d_c:], rows, lists[b, :n], cfg.scale)
+            e_o = rel_err(o_lat[b], ref_o)
+            e_l = np.abs(lse[b] - ref_l).max() / max(np.abs(ref_l).max(), 1.0)
+            say(f"sparse paged={paged} s={splits} b={b} n={n} o_lat {e_o:.2e} lse {e_l:.2e}")
+            assert e_o <= tol(cfg) and e_l <= tol(cfg), (splits, b, e_o, e_l)
+            if n == 1:   # one listed row: its latent, exactly
+                row = rows[lists[b, 0], :cfg.d_c]
+                assert np.array_equal(o_lat[b], np.broadcast_to(row, o_lat[b].shape)), (splits, b)
+
+
+def test_sparse_full_list_equals_dense_bitwise():
+    """Listing every row in order is dense attention: same chunks, same
+    arithmetic, identical bits."""
+    cfg = V3.with_(name="v3_sparse_full", B=3, ctx=(700, 64, 1500), seed=24)
+    inp = make_inputs(cfg)
+    q = gen.make_query(cfg)
+    fill_append_slots(inp)
+    L = inp.seq_lens.astype(np.int32)
+    lists = np.full((cfg.B, int(L.max())), -1, dtype=np.int32)
+    for b in range(cfg.B):
+        lists[b, :L[b]] = np.arange(L[b])
+    for splits in (0, 3):
+        dense = attention_only(inp, q, splits)
+        sparse = sparse_only(inp, q, lists, L.copy(), splits)
+        assert np.array_equal(dense.host(dense.o_lat), sparse.host(sparse.o_lat)), splits
+        assert np.array_equal(dense.host(dense.lse), sparse.host(sparse.lse)), splits
+
+
 @pytest.mark.parametrize("name,seqs,unabs", [
     ("v3_b1_ctx4k", [0], True),
     ("v3_b64_ctx8k", [0, 63], False),
     ("v3_b8_ctx32k", [3], False),
     ("v3_b128_ragged_paged", None, False),
     ("v3_b64_ctx8k_norm", [5], False),
+    ("v3_b64_ctx8k_topk2048", [0, 63], False),
 ])
 def test_full_size_configs_sampled(name, seqs, unabs):
     """The configured workloads at full size, in the launch configuration the

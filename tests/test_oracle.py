@@ -350,3 +350,82 @@ def test_generator_history_of_the_normalised_variant():
     # the stored latent rows then have RMS close to that of gamma
     rms = np.sqrt(np.mean(rows[:, :cfg.d_c] ** 2, axis=1))
     assert abs(np.median(rms) - np.sqrt(np.mean(g ** 2))) < 0.05
+
+
+# --- sparse attention over a listed top-k subset ([KB] section 4) ---
+
+def _tiny_attention_inputs(seed=7, L=40):
+    rng = np.random.default_rng(seed)
+    H, d_c, d_R = 4, 32, 8
+    q_lat = rng.standard_normal((H, d_c))
+    qR = rng.standard_normal((H, d_R))
+    rows = rng.standard_normal((L, d_c + d_R))
+    return q_lat, qR, rows, 1.0 / math.sqrt(24)
+
+
+def test_sparse_attention_is_a_masked_softmax_brute_force():
+    """Against pure-Python loops: softmax over all rows with every unlisted
+    row's weight set to zero, normalised over the listed ones."""
+    q_lat, qR, rows, scale = _tiny_attention_inputs()
+    idx = [31, 2, 17, 5, 39, 0, 22]
+    o, lse = om.attend_sparse(q_lat, qR, rows, idx, scale)
+    H, d_c = q_lat.shape
+    for i in range(H):
+        sc = {}
+        for u in idx:
+            dot = sum(q_lat[i, c] * rows[u, c] for c in range(d_c))
+            dot += sum(qR[i, j] * rows[u, d_c + j] for j in range(qR.shape[1]))
+            sc[u] = dot * scale
+        m = max(sc.values())
+        w = {u: math.exp(v - m) for u, v in sc.items()}
+        z = sum(w.values())
+        for c in range(d_c):
+            ref = sum(w[u] * rows[u, c] for u in idx) / z
+            assert abs(o[i, c] - ref) < 1e-12
+        assert abs(lse[i] - (m + math.log(z))) < 1e-12
+
+
+def test_sparse_attention_order_single_row_and_empty():
+    q_lat, qR, rows, scale = _tiny_attention_inputs(seed=8)
+    idx = np.array([3, 11, 29, 7, 0, 35])
+    o1, l1 = om.attend_sparse(q_lat, qR, rows, idx, scale)
+    o2, l2 = om.attend_sparse(q_lat, qR, rows, idx[::-1].copy(), scale)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13)
+    # one listed row: its latent exactly, lse = its score
+    o, l = om.attend_sparse(q_lat, qR, rows, [13], scale)
+    assert np.array_equal(o, np.broadcast_to(rows[13, :32], o.shape))
+    np.testing.assert_allclose(l, (q_lat @ rows[13, :32] + qR @ rows[13, 32:]) * scale, rtol=1e-13)
+    # the whole list in order equals dense attention over every row
+    oa, la = om.attend_absorbed(q_lat, qR, rows, scale)
+    ob, lb = om.attend_sparse(q_lat, qR, rows, np.arange(rows.shape[0]), scale)
+    np.testing.assert_allclose(ob, oa, rtol=1e-13, atol=1e-14)
+    # an empty list: zeros and -inf
+    o, l = om.attend_sparse(q_lat, qR, rows, [], scale)
+    assert not o.any() and np.all(np.isneginf(l))
+
+
+def test_sparse_decode_step_absorbed_equals_unabsorbed():
+    """The absorption identity ([DONG] section 4) holds on a listed subset."""
+    cfg = small_v3(B=1, ctx=(300,), seed=4)
+    inp = make_inputs(cfg)
+    W = {k: (None if v is None else gen.to_f64(v, cfg.dtype)) for k, v in inp.weights.items()}
+    h = gen.to_f64(inp.h_t[0], cfg.dtype)
+    prior = gen.to_f64(inp.rows(0, 300), cfg.dtype)
+    idx = np.random.default_rng(2).choice(301, size=64, replace=False)
+    u = om.decode_step(h, prior, W, 300, cfg.theta, cfg.scale, cfg.dtype, idx=idx)
+    a = om.decode_step_absorbed(h, prior, W, 300, cfg.theta, cfg.scale, cfg.dtype, idx=idx)
+    np.testing.assert_allclose(a["o"], u["o"], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(a["out"], u["out"], rtol=1e-9, atol=1e-12)
+
+
+def test_topk_lists_are_distinct_positions_in_range():
+    cfg = gen.CONFIGS["v3_b64_ctx8k_topk2048"].with_(B=3, ctx=(100, 5000, 2047))
+    seq_lens = np.array([101, 5001, 2048])
+    idx, counts = gen.make_topk_indices(cfg, seq_lens, 2048)
+    assert counts.tolist() == [101, 2048, 2048]
+    for b in range(3):
+        n = int(counts[b])
+        listed = idx[b, :n]
+        assert len(set(listed.tolist())) == n and listed.min() >= 0 and listed.max() < seq_lens[b]
+        assert (idx[b, n:] == -1).all()
