@@ -9,11 +9,15 @@ synthetic tensors of the DeepSeek-V3 geometry, resident in HBM before timing.
 Headline: decode-attention TFLOP/s (algorithmic FLOPs 2*H*(D + d_c) per
 attended row) and latent-cache GB/s (1152 B per attended row) of the
 mla_decode_attn call, both from HIP events recorded on the stream the library
-launches on; ms_per_step is the whole step. The roofline object prices the
+launches on; ms_per_step is the whole step and calls_ms the mean time of each
+of the four calls (events between them). The roofline object prices the
 attention call against MI355X's published HBM bandwidth (8 TB/s); the CPU
 baseline times the float64 oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--precomposed]
+--precomposed runs the query and output sides with the composed weights
+W_QK = W_UK^T W_UQ and W_OV = W_O blockdiag(W_UV), formed before timing.
 """
 import argparse
 import hashlib
@@ -102,6 +106,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--precomposed", action="store_true",
+                    help="query and output sides with composed weights W_QK, W_OV (formed before timing)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path is "
@@ -122,30 +128,37 @@ def main():
     t0 = time.perf_counter()
     inp = gen.make_inputs(cfg)
     log(f"inputs for {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
-    st = DeviceStep(inp, num_splits=args.num_splits)
+    st = DeviceStep(inp, num_splits=args.num_splits, precomposed=args.precomposed)
     attended = st.topk_counts_host if cfg.topk else inp.seq_lens
     rows, cache_bytes, attn_bytes, attn_flops = attn_work(cfg, attended)
     splits = st.splits
     log(f"B={cfg.B} rows={rows} splits={splits} kernel={mla.decode_kernel(st.dims)}")
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # events between the four calls, all on the stream the library launches on
+    calls = ("compress_append", "absorb_q", "decode_attn", "out_proj")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
 
     t_start = time.perf_counter()
     for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
         st.compress_append()
+        e[1].record(stream)
         st.absorb_q()
-        ev[k][0].record(stream)
+        e[2].record(stream)
         st.decode_attn()
-        ev[k][1].record(stream)
+        e[3].record(stream)
         st.out_proj()
+        e[4].record(stream)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    calls_ms = {c: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])), 5)
+                for i, c in enumerate(calls)}
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     ms_per_step = t_total * 1e3 / args.steps
 
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
@@ -167,8 +180,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "ctx": int(inp.ctx.max()),
                    "rows_attended": rows, "heads": cfg.H, "d_c": cfg.d_c, "d_R": cfg.d_R,
-                   "paged": cfg.paged, "num_splits": splits, "topk": cfg.topk},
+                   "paged": cfg.paged, "num_splits": splits, "topk": cfg.topk,
+                   "precomposed": bool(args.precomposed)},
         "attn_ms": round(attn_ms, 5),
+        "calls_ms": calls_ms,
         "cache_GBps": round(cache_gbps, 1),
         "pct_hbm_roofline": round(100 * achieved_gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,

@@ -211,6 +211,57 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat,
                         const void* W_UV, const void* W_O, void* o_heads,
                         void* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Precomposed weights ([KB] section 3, "the core trick": the key
+ * up-projection folded into the query-side matrix once, offline; [CASS]
+ * "absorbed-weights box": the value up-projection pre-multiplied into the
+ * output projection). The per-head products are formed once:
+ *   W_QK(i) = W_UK(i)^T W_UQ(i)   [H][d_c][qin]   (qin = d_cq, or d if 0)
+ *   W_OV    = W_O blockdiag(W_UV(1), ..., W_UV(H))   [d][H*d_c]
+ *             i.e. W_OV[:, i*d_c:(i+1)*d_c] = W_O[:, i*d_v:(i+1)*d_v] W_UV(i)
+ * and the decode step then uses one product per side. The results equal
+ * those of mla_absorb_q / mla_out_proj up to rounding: the composed weights
+ * are rounded once to the storage dtype, and the two-step path instead
+ * rounds the intermediate q_C and o_heads. Which is faster depends on the
+ * sizes: the composed weights are d_c/d_h (query) and H*d_c/(H*d_v) (output)
+ * times the per-head up-projections they replace, so they pay off only when
+ * the batch is large enough for the product to be compute-bound.
+ */
+
+/*
+ * mla_precompose -- form W_QK and (if W_UV, W_O and W_OV are all given) W_OV.
+ * Accumulates in float32 and rounds once to the storage dtype (nearest-even).
+ *   W_UQ [H][d_h][qin], W_UK [H][d_h][d_c], W_UV [H][d_v][d_c], W_O [d][H*d_v]
+ *   W_QK [H][d_c][qin] out;  W_OV [d][H*d_c] out, or NULL with W_UV, W_O NULL
+ * Needs no workspace. Errors: MLA_ERR_NULL if W_UQ, W_UK or W_QK is NULL or
+ * only some of W_UV, W_O, W_OV are given.
+ */
+mla_status mla_precompose(const mla_dims* dims, const void* W_UQ, const void* W_UK,
+                          const void* W_UV, const void* W_O, void* W_QK, void* W_OV,
+                          void* stream);
+
+/*
+ * mla_absorb_q_precomposed -- the absorbed query from precomposed weights:
+ *   c_Q      = W_DQ h_t[b]          (h_t[b] when d_cq == 0, W_DQ NULL)
+ *   q_lat(i) = W_QK(i) c_Q
+ *   q_R(i)   = RoPE(W_QR(i) c_Q, pos[b])
+ * Output q [B][H][d_c + d_R] exactly as mla_absorb_q lays it out.
+ * ws: mla_workspace_bytes(dims, B, ...) bytes suffice.
+ */
+mla_status mla_absorb_q_precomposed(const mla_dims* dims, int32_t B, const void* h_t,
+                                    const void* W_DQ, const void* W_QK, const void* W_QR,
+                                    const int32_t* pos, void* q, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/*
+ * mla_out_proj_precomposed -- out(b) = W_OV o_lat(b), o_lat [B][H][d_c]
+ * float32 read as [B][H*d_c]; out [B][d] storage dtype. No per-head outputs.
+ * ws: mla_workspace_bytes(dims, B, ...) bytes suffice.
+ */
+mla_status mla_out_proj_precomposed(const mla_dims* dims, int32_t B, const float* o_lat,
+                                    const void* W_OV, void* out, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* Workspace bytes that suffice for every call above with these sizes
  * (num_splits as passed to mla_decode_attn, 0 = automatic). 0 on bad dims. */
 size_t mla_workspace_bytes(const mla_dims* dims, int32_t B, int32_t max_seq_len,

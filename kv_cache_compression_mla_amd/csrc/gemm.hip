@@ -565,6 +565,26 @@ __global__ __launch_bounds__(1024) void append_kernel(const float* __restrict__ 
   }
 }
 
+// Offline weight composition, C(g, m, n) = sum_k X(g, k, m) Y(g, k, n), with
+// element strides X(g, k, m) = X[g*xg + k*xk + m*xm], Y(g, k, n) =
+// Y[g*yg + k*yk + n], C(g, m, n) = C[g*cg + m*cm + n]; fp32 accumulation,
+// one thread per output element, the X value shared by the workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void compose_kernel(const T* __restrict__ X, long long xg, long long xk,
+                                                      long long xm, const T* __restrict__ Y, long long yg,
+                                                      long long yk, T* __restrict__ C, long long cg, long long cm,
+                                                      int N, int K) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int m = blockIdx.y;
+  const int g = blockIdx.z;
+  if (n >= N) return;
+  const T* x = X + g * xg + m * xm;
+  const T* y = Y + g * yg + n;
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k) acc += Elem<T>::ld(x + k * xk) * Elem<T>::ld(y + k * yk);
+  Elem<T>::st(C + g * cg + m * cm + n, acc);
+}
+
 bool mfma_ok(const GemmArgs& a) {
   if (a.dtype != MLA_BF16) return false;
   if (a.K % 8 || a.lda % 8 || a.ldw % 8 || a.sAg % 8 || a.sWg % 8) return false;
@@ -724,5 +744,20 @@ hipError_t launch_append(const float* Pc, int splits_c, int ldc, const float* Pr
   return hipGetLastError();
 }
 
+
+hipError_t launch_compose(const void* X, long long xg, long long xk, long long xm, const void* Y, long long yg,
+                          long long yk, void* C, long long cg, long long cm, int G, int M, int N, int K, int dtype,
+                          hipStream_t stream) {
+  const dim3 grid((N + 255) / 256, M, G);
+  if (dtype == MLA_BF16)
+    compose_kernel<uint16_t><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(X), xg, xk, xm,
+                                                       static_cast<const uint16_t*>(Y), yg, yk,
+                                                       static_cast<uint16_t*>(C), cg, cm, N, K);
+  else
+    compose_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(X), xg, xk, xm,
+                                                    static_cast<const float*>(Y), yg, yk, static_cast<float*>(C),
+                                                    cg, cm, N, K);
+  return hipGetLastError();
+}
 
 }  // namespace mla

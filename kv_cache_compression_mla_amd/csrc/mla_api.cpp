@@ -174,6 +174,19 @@ size_t ws_attn(const mla_dims* d, int B, int max_seq_len, int num_splits) {
          align_up(static_cast<size_t>(B) * s * d->H * 2 * sizeof(float));
 }
 
+// precomposed variant: c_Q, then partials of W_DQ, of the per-head W_QK
+// product and of W_QR; the output product over H*d_c inputs
+size_t ws_absorb_pre(const mla_dims* d, int B) {
+  const size_t es = elem_size(d->dtype);
+  const int qin = d->d_cq ? d->d_cq : d->d;
+  size_t p = 0;
+  if (d->d_cq) p = part_bytes({B, d->d_cq, d->d, 1}, d->dtype);
+  p = std::max(p, part_bytes({B, d->d_c, qin, d->H}, d->dtype));
+  p = std::max(p, part_bytes({B, d->H * d->d_R, qin, 1}, d->dtype));
+  return align_up(static_cast<size_t>(B) * d->d_cq * es) + align_up(p);
+}
+size_t ws_out_pre(const mla_dims* d, int B) { return align_up(part_bytes({B, d->d, d->H * d->d_c, 1}, d->dtype)); }
+
 size_t ws_out(const mla_dims* d, int B) {
   return align_up(std::max(part_bytes({B, d->d_v, d->d_c, d->H}, d->dtype),
                            part_bytes({B, d->d, d->H * d->d_v, 1}, d->dtype)));
@@ -259,6 +272,8 @@ size_t mla_workspace_bytes(const mla_dims* dims, int32_t B, int32_t max_seq_len,
   w = std::max(w, ws_absorb(dims, B));
   w = std::max(w, ws_attn(dims, B, max_seq_len, num_splits));
   w = std::max(w, ws_out(dims, B));
+  w = std::max(w, ws_absorb_pre(dims, B));
+  w = std::max(w, ws_out_pre(dims, B));
   return std::max<size_t>(w, 256);
 }
 
@@ -466,6 +481,99 @@ mla_status mla_decode_attn_sparse(const mla_dims* dims, int32_t B, const void* q
     return fail(MLA_ERR_ALIGN, "decode_attn_sparse: indices and counts must be 4-byte aligned");
   return decode_attn_impl(dims, B, q, cache, counts, topk, num_splits, o_lat, lse, ws, ws_bytes, stream, indices,
                           topk);
+}
+
+mla_status mla_precompose(const mla_dims* dims, const void* W_UQ, const void* W_UK, const void* W_UV,
+                          const void* W_O, void* W_QK, void* W_OV, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (!W_UQ || !W_UK || !W_QK) return fail(MLA_ERR_NULL, "precompose: NULL W_UQ, W_UK or W_QK");
+  if ((W_OV != nullptr) != (W_UV != nullptr && W_O != nullptr) || ((W_UV == nullptr) != (W_O == nullptr)))
+    return fail(MLA_ERR_NULL, "precompose: W_UV, W_O and W_OV must all be given or all be NULL");
+  for (const void* p : {W_UQ, W_UK, static_cast<const void*>(W_QK), W_UV, W_O, static_cast<const void*>(W_OV)})
+    if (p && !aligned16(p)) return fail(MLA_ERR_ALIGN, "precompose: pointer not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = dims->dtype;
+  const int H = dims->H, d_h = dims->d_h, d_v = dims->d_v, d_c = dims->d_c;
+  const int qin = dims->d_cq ? dims->d_cq : dims->d;
+  // W_QK(i)[m][n] = sum_k W_UK(i)[k][m] W_UQ(i)[k][n]
+  MLA_TRY(hip_status(mla::launch_compose(W_UK, static_cast<long long>(d_h) * d_c, d_c, 1, W_UQ,
+                                         static_cast<long long>(d_h) * qin, qin, W_QK,
+                                         static_cast<long long>(d_c) * qin, qin, H, d_c, qin, d_h, dt, st),
+                     "compose launch"));
+  if (W_OV) {
+    // W_OV[r][i*d_c + n] = sum_k W_O[r][i*d_v + k] W_UV(i)[k][n]
+    MLA_TRY(hip_status(mla::launch_compose(W_O, d_v, 1, static_cast<long long>(H) * d_v, W_UV,
+                                           static_cast<long long>(d_v) * d_c, d_c, W_OV, d_c,
+                                           static_cast<long long>(H) * d_c, H, dims->d, d_c, d_v, dt, st),
+                       "compose launch"));
+  }
+  return ok();
+}
+
+mla_status mla_absorb_q_precomposed(const mla_dims* dims, int32_t B, const void* h_t, const void* W_DQ,
+                                    const void* W_QK, const void* W_QR, const int32_t* pos, void* q, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
+  if (!h_t || !W_QK || !W_QR || !pos || !q || !ws) return fail(MLA_ERR_NULL, "absorb_q_precomposed: NULL pointer");
+  if ((dims->d_cq != 0) != (W_DQ != nullptr))
+    return fail(MLA_ERR_NULL, "absorb_q_precomposed: W_DQ must be given iff d_cq > 0");
+  for (const void* p : {h_t, W_QK, W_QR, static_cast<const void*>(pos), static_cast<const void*>(q),
+                        static_cast<const void*>(ws)})
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "absorb_q_precomposed: pointer not 16-byte aligned");
+  if (W_DQ && !aligned16(W_DQ)) return fail(MLA_ERR_ALIGN, "absorb_q_precomposed: W_DQ not 16-byte aligned");
+  const size_t need = ws_absorb_pre(dims, B);
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "absorb_q_precomposed needs %zu bytes", need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = dims->dtype;
+  const size_t es = elem_size(dt);
+  const bool f32 = dt == MLA_FP32;
+  const int H = dims->H, d_R = dims->d_R, d_c = dims->d_c, D = d_c + d_R;
+  char* w = static_cast<char*>(ws);
+  void* cq = w;
+  float* P = reinterpret_cast<float*>(w + align_up(static_cast<size_t>(B) * dims->d_cq * es));
+  const void* cin = h_t;
+  int qin = dims->d;
+  if (dims->d_cq) {
+    const GemmShape s{B, dims->d_cq, dims->d, 1};
+    MLA_TRY(gemm_store(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, cq, dims->d_cq, 0, st));
+    cin = cq;
+    qin = dims->d_cq;
+  }
+  // q_lat(i) = W_QK(i) c_Q: one activation row per sequence shared by all heads
+  {
+    const GemmShape s{B, d_c, qin, H};
+    MLA_TRY(gemm_store(cin, qin, 0, f32, W_QK, qin, static_cast<long long>(d_c) * qin, false, s, dt, P, q,
+                       static_cast<long long>(H) * D, D, st));
+  }
+  // q_R(i) = RoPE(W_QR(i) c_Q, pos), as in mla_absorb_q
+  {
+    const GemmShape s{B, H * d_R, qin, 1};
+    MLA_TRY(gemm(cin, qin, 0, f32, W_QR, qin, 0, false, s, dt, P, st));
+    void* qr = static_cast<char*>(q) + static_cast<size_t>(d_c) * es;
+    MLA_TRY(hip_status(mla::launch_reduce_rope(P, splits_for(s, dt), B, H, d_R, pos, dims->rope_theta, qr,
+                                               static_cast<long long>(H) * D, D, dt, st),
+                       "rope launch"));
+  }
+  return ok();
+}
+
+mla_status mla_out_proj_precomposed(const mla_dims* dims, int32_t B, const float* o_lat, const void* W_OV, void* out,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
+  if (!o_lat || !W_OV || !out || !ws) return fail(MLA_ERR_NULL, "out_proj_precomposed: NULL pointer");
+  for (const void* p : {static_cast<const void*>(o_lat), W_OV, static_cast<const void*>(out),
+                        static_cast<const void*>(ws)})
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "out_proj_precomposed: pointer not 16-byte aligned");
+  const size_t need = ws_out_pre(dims, B);
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "out_proj_precomposed needs %zu bytes", need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = dims->dtype;
+  const long long K = static_cast<long long>(dims->H) * dims->d_c;
+  // out(b) = W_OV o_lat(b) over all heads' latents at once
+  const GemmShape s{B, dims->d, static_cast<int>(K), 1};
+  return gemm_store(o_lat, K, 0, true, W_OV, K, 0, false, s, dt, static_cast<float*>(ws), out, dims->d, 0, st);
 }
 
 mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat, const void* W_UV, const void* W_O,

@@ -105,6 +105,12 @@ hipError_t launch_append(const float* Pc, int splits_c, int ldc, const float* Pr
                          int d_c, int d_R, const void* gamma, float eps, const int32_t* pos,
                          float theta, const mla_cache& cache, int dtype, hipStream_t stream);
 
+// Offline composition C(g, m, n) = sum_k X(g, k, m) Y(g, k, n) with element
+// strides (see gemm.hip); fp32 accumulation, stored in dtype.
+hipError_t launch_compose(const void* X, long long xg, long long xk, long long xm, const void* Y, long long yg,
+                          long long yk, void* C, long long cg, long long cm, int G, int M, int N, int K, int dtype,
+                          hipStream_t stream);
+
 // Attention. chunk = rows per split (multiple of 32 for the MFMA kernel).
 struct AttnArgs {
   const void* q;

@@ -54,6 +54,11 @@ _SIGS = {
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_out_proj": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32] + [ctypes.c_void_p] * 6
                      + [ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_precompose": (ctypes.c_int, [ctypes.POINTER(MLADims)] + [ctypes.c_void_p] * 7),
+    "mla_absorb_q_precomposed": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32] + [ctypes.c_void_p] * 7
+                                 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_out_proj_precomposed": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32] + [ctypes.c_void_p] * 4
+                                 + [ctypes.c_size_t, ctypes.c_void_p]),
     "mla_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32]),
     "mla_decode_num_splits": (ctypes.c_int32, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
@@ -191,3 +196,28 @@ def mla_out_proj(dims, o_lat, W_UV, W_O, o_heads, out, ws, stream=None):
         ctypes.byref(dims), B, _ptr(o_lat, torch.float32, "o_lat"), _ptr(W_UV, dt, "W_UV"),
         _ptr(W_O, dt, "W_O"), _ptr(o_heads, dt, "o_heads"), _ptr(out, dt, "out"),
         _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)), "mla_out_proj")
+
+
+def mla_precompose(dims, W_UQ, W_UK, W_QK, W_UV=None, W_O=None, W_OV=None, stream=None):
+    """W_QK(i) = W_UK(i)^T W_UQ(i); W_OV = W_O blockdiag(W_UV(i)) when W_UV, W_O, W_OV are given."""
+    dt = dims.torch_dtype
+    _check(lib().mla_precompose(
+        ctypes.byref(dims), _ptr(W_UQ, dt, "W_UQ"), _ptr(W_UK, dt, "W_UK"), _ptr(W_UV, dt, "W_UV"),
+        _ptr(W_O, dt, "W_O"), _ptr(W_QK, dt, "W_QK"), _ptr(W_OV, dt, "W_OV"), _stream(stream)), "mla_precompose")
+
+
+def mla_absorb_q_precomposed(dims, h_t, W_DQ, W_QK, W_QR, pos, q, ws, stream=None):
+    dt = dims.torch_dtype
+    B = h_t.shape[0]
+    _check(lib().mla_absorb_q_precomposed(
+        ctypes.byref(dims), B, _ptr(h_t, dt, "h_t"), _ptr(W_DQ, dt, "W_DQ"), _ptr(W_QK, dt, "W_QK"),
+        _ptr(W_QR, dt, "W_QR"), _ptr(pos, torch.int32, "pos"), _ptr(q, dt, "q"), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)), "mla_absorb_q_precomposed")
+
+
+def mla_out_proj_precomposed(dims, o_lat, W_OV, out, ws, stream=None):
+    dt = dims.torch_dtype
+    B = o_lat.shape[0]
+    _check(lib().mla_out_proj_precomposed(
+        ctypes.byref(dims), B, _ptr(o_lat, torch.float32, "o_lat"), _ptr(W_OV, dt, "W_OV"), _ptr(out, dt, "out"),
+        _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)), "mla_out_proj_precomposed")

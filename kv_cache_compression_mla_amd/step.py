@@ -27,8 +27,10 @@ def to_device(a: Optional[np.ndarray], dtype: str, device="cuda") -> Optional[to
 
 
 class DeviceStep:
-    def __init__(self, inp: MLAInputs, num_splits: int = 0, device="cuda", ws_splits=()):
-        """ws_splits: further split counts the workspace must also cover."""
+    def __init__(self, inp: MLAInputs, num_splits: int = 0, device="cuda", ws_splits=(), precomposed=False):
+        """ws_splits: further split counts the workspace must also cover.
+        precomposed: form W_QK and W_OV once here and run the query and output
+        sides as one product each (no per-head outputs then)."""
         cfg = inp.cfg
         self.cfg, self.inp, self.device = cfg, inp, device
         self.num_splits = num_splits
@@ -60,6 +62,13 @@ class DeviceStep:
         self.lse = torch.empty(B, H, dtype=torch.float32, device=device)
         self.o_heads = torch.empty(B, H, cfg.d_v, dtype=tdt, device=device)
         self.out = torch.empty(B, cfg.d, dtype=tdt, device=device)
+        self.precomposed = precomposed
+        if precomposed:
+            qin = cfg.d_cq if cfg.d_cq else cfg.d
+            self.W_QK = torch.empty(H, cfg.d_c, qin, dtype=tdt, device=device)
+            self.W_OV = torch.empty(cfg.d, H * cfg.d_c, dtype=tdt, device=device)
+            mla.mla_precompose(self.dims, self.W["W_UQ"], self.W["W_UK"], self.W_QK, self.W["W_UV"],
+                               self.W["W_O"], self.W_OV)
 
     @property
     def splits(self) -> int:
@@ -71,6 +80,10 @@ class DeviceStep:
                                 self.W.get("gamma_kv"), self.pos, self.cdesc, self.ws)
 
     def absorb_q(self):
+        if self.precomposed:
+            mla.mla_absorb_q_precomposed(self.dims, self.h_t, self.W["W_DQ"], self.W_QK, self.W["W_QR"],
+                                         self.pos, self.q, self.ws)
+            return
         mla.mla_absorb_q(self.dims, self.h_t, self.W["W_DQ"], self.W["W_UQ"], self.W["W_QR"],
                          self.W["W_UK"], self.pos, self.q, self.ws)
 
@@ -84,6 +97,9 @@ class DeviceStep:
                                 self.o_lat, self.lse, self.ws, s)
 
     def out_proj(self):
+        if self.precomposed:
+            mla.mla_out_proj_precomposed(self.dims, self.o_lat, self.W_OV, self.out, self.ws)
+            return
         mla.mla_out_proj(self.dims, self.o_lat, self.W["W_UV"], self.W["W_O"], self.o_heads,
                          self.out, self.ws)
 

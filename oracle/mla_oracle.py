@@ -227,6 +227,53 @@ def expand_out(o_lat, W_UV) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Precomposed weights
+# --------------------------------------------------------------------------
+
+def precompose_qk(W_UQ, W_UK) -> np.ndarray:
+    """W_QK(i) = W_UK(i)^T W_UQ(i) in R^{d_c x qin}, per head.
+
+    [KB] section 3 ("the core trick"): the key up-projection is folded into
+    the query-side matrix once, offline, so the absorbed query comes from one
+    product with c_Q. The printed composite W_UK W_UQ does not chain for
+    W_UK in R^{d_h x d_c}; the transpose on W_UK is the reading (the same one
+    absorb_q takes), which makes q_lat(i) = W_QK(i) c_Q = W_UK(i)^T q_C(i).
+    """
+    W_UQ = np.asarray(W_UQ, dtype=np.float64)
+    W_UK = np.asarray(W_UK, dtype=np.float64)
+    return np.stack([W_UK[i].T @ W_UQ[i] for i in range(W_UQ.shape[0])])
+
+
+def precompose_ov(W_UV, W_O) -> np.ndarray:
+    """W_OV = W_O blockdiag(W_UV(1), ..., W_UV(H)) in R^{d x H*d_c}.
+
+    [CASS] "absorbed-weights box": the value up-projection sits next to the
+    output projection and can be pre-multiplied into it. Head i's block of
+    columns is W_O[:, i*d_v:(i+1)*d_v] W_UV(i), so out = W_OV [o_lat(1); ...;
+    o_lat(H)] equals W_O [W_UV(1) o_lat(1); ...].
+    """
+    W_UV = np.asarray(W_UV, dtype=np.float64)
+    W_O = np.asarray(W_O, dtype=np.float64)
+    H, d_v, d_c = W_UV.shape
+    return np.concatenate([W_O[:, i * d_v:(i + 1) * d_v] @ W_UV[i] for i in range(H)], axis=1)
+
+
+def query_precomposed(h, W_DQ, W_QK, W_QR, pos: int, theta: float):
+    """(q_lat [H][d_c], q_R [H][d_R]) from precomposed W_QK: q_lat(i) = W_QK(i) c_Q,
+    the rotary part as in query()."""
+    h = np.asarray(h, dtype=np.float64)
+    cq = h if W_DQ is None else np.asarray(W_DQ, dtype=np.float64) @ h
+    q_lat = np.einsum("icj,j->ic", np.asarray(W_QK, dtype=np.float64), cq)
+    qR = rope(np.einsum("ikj,j->ik", np.asarray(W_QR, dtype=np.float64), cq), pos, theta)
+    return q_lat, qR
+
+
+def out_proj_precomposed(o_lat, W_OV) -> np.ndarray:
+    """out = W_OV [o_lat(1); ...; o_lat(H)]."""
+    return np.asarray(W_OV, dtype=np.float64) @ np.asarray(o_lat, dtype=np.float64).reshape(-1)
+
+
+# --------------------------------------------------------------------------
 # Whole step for one sequence
 # --------------------------------------------------------------------------
 

@@ -138,3 +138,23 @@ def test_workspace_covers_every_call():
     for dims, B, L_ in ((v3(), 64, 8193), (v3(), 8, 32769), (v3(), 128, 16385), (tiny(), 1, 65)):
         for s in (0, 1, 2, 8):
             assert mla.workspace_bytes(dims, B, L_, s) > 0
+
+
+def test_precomposed_argument_errors(L):
+    d = v3()
+    need = L.mla_workspace_bytes(ctypes.byref(d), 4, 100, 0)
+    # precompose: the output side all or nothing
+    p = lambda uq=A, uk=A, uv=A, wo=A, qk=A, ov=A: L.mla_precompose(ctypes.byref(d), uq, uk, uv, wo, qk, ov, None)
+    assert p(uq=None) == NULL and p(uk=None) == NULL and p(qk=None) == NULL
+    assert p(ov=None) == NULL and p(uv=None) == NULL and p(wo=None, ov=None) == NULL
+    assert p(qk=MIS) == ALIGN and p(ov=MIS) == ALIGN
+    assert L.mla_precompose(None, A, A, A, A, A, A, None) == NULL
+    # absorb_q_precomposed
+    g = lambda dq=A, dims=d, wsb=need, qq=A, qk=A: L.mla_absorb_q_precomposed(ctypes.byref(dims), 4, A, dq, qk, A,
+                                                                             A, qq, A, wsb, None)
+    assert g(dq=None) == NULL and g(dims=v3(d_cq=0), dq=A) == NULL
+    assert g(qk=None) == NULL and g(qq=MIS) == ALIGN and g(wsb=1) == WORKSPACE
+    assert L.mla_absorb_q_precomposed(ctypes.byref(d), 0, A, A, A, A, A, A, A, need, None) == SHAPE
+    # out_proj_precomposed
+    h = lambda ov=A, out=A, wsb=need: L.mla_out_proj_precomposed(ctypes.byref(d), 4, A, ov, out, A, wsb, None)
+    assert h(ov=None) == NULL and h(out=None) == NULL and h(out=MIS) == ALIGN and h(wsb=1) == WORKSPACE

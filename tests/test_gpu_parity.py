@@ -73,7 +73,8 @@ def check_step(inp, st, seqs=None, unabsorbed=True, label=""):
     q = st.host(st.q)
     o_lat = st.host(st.o_lat)
     lse = st.host(st.lse)
-    o_heads = st.host(st.o_heads)
+    pre = getattr(st, "precomposed", False)      # no per-head outputs then
+    o_heads = None if pre else st.host(st.o_heads)
     out = st.host(st.out)
     for b in seqs:
         r = oracle_seq(inp, W, b, absorbed=True, unabsorbed=unabsorbed)
@@ -84,7 +85,7 @@ def check_step(inp, st, seqs=None, unabsorbed=True, label=""):
         e_olat = rel_err(o_lat[b], a["o_lat"])
         e_lse = np.abs(lse[b] - a["lse"]).max() / max(np.abs(a["lse"]).max(), 1.0)
         ref = r["unabs"] if unabsorbed else a
-        e_o = rel_err(o_heads[b], ref["o"])
+        e_o = 0.0 if pre else rel_err(o_heads[b], ref["o"])
         e_out = rel_err(out[b], ref["out"])
         say(f"{label} b={b} L={int(inp.seq_lens[b])} row {e_row:.2e} q {e_q:.2e} o_lat {e_olat:.2e} "
             f"lse {e_lse:.2e} o {e_o:.2e} out {e_out:.2e}")
@@ -386,3 +387,71 @@ def test_full_size_configs_sampled(name, seqs, unabs):
     # every sequence's latent output is finite and its lse is consistent in size
     assert np.isfinite(st.host(st.o_lat)).all()
     assert np.isfinite(st.host(st.lse)).all()
+
+
+# --------------------------------------------------------------------------
+# Precomposed weights
+# --------------------------------------------------------------------------
+
+def composed_weight_err(got, ref, dtype):
+    """Largest |got - ref| over the bound one rounding to the storage dtype plus
+    float32 accumulation allows: half an ulp of bf16 (2^-9 relative) or of
+    float32, plus 1e-5 of the largest entry for sums that cancel."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -22
+    bound = rel * np.abs(ref) + 1e-5 * np.abs(ref).max()
+    return float((np.abs(got - ref) / bound).max())
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "tiny_fp32_cq", "v3_small"])
+def test_precomposed_weights_and_step_against_oracle(name):
+    """mla_precompose against the oracle's float64 composition entry by entry,
+    then a step with the composed weights (one query product, one output
+    product) against the unabsorbed definition."""
+    if name == "tiny_fp32":
+        cfg = gen.CONFIGS["tiny_fp32"]
+    elif name == "tiny_fp32_cq":
+        cfg = gen.CONFIGS["tiny_fp32"].with_(name="tiny_fp32_cq", ctx=(9, 40), B=2, d_cq=24, seed=2)
+    else:
+        cfg = V3.with_(name="v3_small", B=3, ctx=(0, 45, 300))
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    st = DeviceStep(inp, precomposed=True)
+    say(f"precomposed {name} B={cfg.B} dtype={cfg.dtype}")
+    torch.cuda.synchronize()
+    QK = om.precompose_qk(W["W_UQ"], W["W_UK"])
+    e = composed_weight_err(st.host(st.W_QK), QK, cfg.dtype)
+    say(f"  W_QK {e:.3f} of the bound")
+    assert e <= 1.0
+    rows = np.random.default_rng(0).choice(cfg.d, size=min(cfg.d, 96), replace=False)
+    OV = om.precompose_ov(W["W_UV"], W["W_O"][rows])
+    e = composed_weight_err(st.host(st.W_OV)[rows], OV, cfg.dtype)
+    say(f"  W_OV {e:.3f} of the bound (rows sampled)")
+    assert e <= 1.0
+    st.run()
+    torch.cuda.synchronize()
+    check_step(inp, st, unabsorbed=True, label=f"precomposed {name}")
+
+
+def test_precomposed_full_size_sampled():
+    """The headline workload (64 sequences of 8192 cached rows) with composed
+    weights: sampled sequences against the oracle, and the whole batch within
+    the storage tolerance of the two-step path."""
+    cfg = gen.CONFIGS["v3_b64_ctx8k"]
+    inp = make_inputs(cfg)
+    st = DeviceStep(inp, precomposed=True)
+    say(f"precomposed v3_b64_ctx8k splits={st.splits}")
+    st.run()
+    torch.cuda.synchronize()
+    check_step(inp, st, seqs=[0, 63], unabsorbed=False, label="precomposed v3_b64_ctx8k")
+    out_pre, q_pre = st.host(st.out), st.host(st.q)
+    del st
+    two = DeviceStep(inp)
+    two.run()
+    torch.cuda.synchronize()
+    for a, b, what in ((q_pre, two.host(two.q), "q"), (out_pre, two.host(two.out), "out")):
+        e = rel_err(a, b)
+        say(f"  precomposed vs two-step {what}: {e:.2e}")
+        assert e <= tol(cfg), (what, e)

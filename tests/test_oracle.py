@@ -429,3 +429,82 @@ def test_topk_lists_are_distinct_positions_in_range():
         listed = idx[b, :n]
         assert len(set(listed.tolist())) == n and listed.min() >= 0 and listed.max() < seq_lens[b]
         assert (idx[b, n:] == -1).all()
+
+
+# --------------------------------------------------------------------------
+# Precomposed weights
+# --------------------------------------------------------------------------
+
+def test_precomposed_weights_entry_by_entry():
+    """W_QK(i)[c][j] = sum_k W_UK(i)[k][c] W_UQ(i)[k][j] and W_OV[r][i*d_c + c] =
+    sum_k W_O[r][i*d_v + k] W_UV(i)[k][c], written as explicit sums over k on
+    a few entries of the tiny geometry."""
+    cfg = gen.CONFIGS["tiny_fp32"].with_(d_cq=24, seed=7)
+    W = weights64(make_inputs(cfg))
+    QK = om.precompose_qk(W["W_UQ"], W["W_UK"])
+    OV = om.precompose_ov(W["W_UV"], W["W_O"])
+    H, d_h, d_c = W["W_UK"].shape
+    d_v = W["W_UV"].shape[1]
+    assert QK.shape == (H, d_c, 24) and OV.shape == (cfg.d, H * d_c)
+    rng = np.random.default_rng(0)
+    for _ in range(40):
+        i, c, j = int(rng.integers(H)), int(rng.integers(d_c)), int(rng.integers(24))
+        ref = sum(W["W_UK"][i][k][c] * W["W_UQ"][i][k][j] for k in range(d_h))
+        assert abs(QK[i, c, j] - ref) <= 1e-14 * max(1.0, abs(ref))
+        r = int(rng.integers(cfg.d))
+        ref = sum(W["W_O"][r][i * d_v + k] * W["W_UV"][i][k][c] for k in range(d_v))
+        assert abs(OV[r, i * d_c + c] - ref) <= 1e-14 * max(1.0, abs(ref))
+
+
+def test_precompose_with_identity_up_projections_returns_the_other_factor():
+    """W_UK(i) = I (d_h = d_c) leaves W_QK = W_UQ; W_UV(i) = I (d_v = d_c) leaves
+    W_OV = W_O."""
+    rng = np.random.default_rng(1)
+    H, d_c, qin, d = 3, 8, 5, 7
+    W_UQ = rng.standard_normal((H, d_c, qin))
+    W_O = rng.standard_normal((d, H * d_c))
+    eye = np.broadcast_to(np.eye(d_c), (H, d_c, d_c))
+    np.testing.assert_array_equal(om.precompose_qk(W_UQ, eye), W_UQ)
+    np.testing.assert_array_equal(om.precompose_ov(eye, W_O), W_O)
+
+
+@pytest.mark.parametrize("cfg", [gen.CONFIGS["tiny_fp32"],
+                                 gen.CONFIGS["tiny_fp32"].with_(ctx=(9,), d_cq=24, seed=2)])
+def test_precomposed_step_matches_brute_force(cfg):
+    """The step with precomposed weights (one query product, latent attention,
+    one output product) gives the unabsorbed definition's out, computed by
+    the pure-Python brute force, to 1e-11 relative."""
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    h = gen.to_f64(inp.h_t[0], cfg.dtype)
+    prior = gen.to_f64(inp.rows(0, int(inp.ctx[0])), cfg.dtype)
+    pos = int(inp.ctx[0])
+    Wl = {k: (None if v is None else v.tolist()) for k, v in W.items()}
+    row, o, out = brute.brute_step(h.tolist(), prior.tolist(), Wl, pos, cfg.theta, cfg.scale,
+                                   lambda v: float(np.float32(v)))
+    QK = om.precompose_qk(W["W_UQ"], W["W_UK"])
+    OV = om.precompose_ov(W["W_UV"], W["W_O"])
+    q_lat, qR = om.query_precomposed(h, W["W_DQ"], QK, W["W_QR"], pos, cfg.theta)
+    rows = np.concatenate([prior.reshape(-1, cfg.D), np.asarray(row)[None, :]], axis=0)
+    o_lat, _ = om.attend_absorbed(q_lat, qR, rows, cfg.scale)
+    got = om.out_proj_precomposed(o_lat, OV)
+    np.testing.assert_allclose(got, np.array(out), rtol=1e-11, atol=1e-12 * np.abs(out).max())
+
+
+def test_precomposed_query_and_output_equal_the_two_step_forms_at_v3_width():
+    """Associativity at the V3 geometry: W_QK c_Q = W_UK^T (W_UQ c_Q) and
+    W_OV o_lat = W_O [W_UV(i) o_lat(i)]_i, to 1e-12 relative in float64."""
+    cfg = small_v3(B=1, ctx=(3,))
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    h = gen.to_f64(inp.h_t[0], cfg.dtype)
+    qC, qR = om.query(h, W["W_DQ"], W["W_UQ"], W["W_QR"], 3, cfg.theta)
+    q_lat, qR2 = om.query_precomposed(h, W["W_DQ"], om.precompose_qk(W["W_UQ"], W["W_UK"]), W["W_QR"], 3,
+                                      cfg.theta)
+    ref = om.absorb_q(qC, W["W_UK"])
+    np.testing.assert_array_equal(qR2, qR)
+    assert np.abs(q_lat - ref).max() <= 1e-12 * np.abs(ref).max()
+    o_lat = np.random.default_rng(3).standard_normal((cfg.H, cfg.d_c))
+    ref = om.out_proj(om.expand_out(o_lat, W["W_UV"]), W["W_O"])
+    got = om.out_proj_precomposed(o_lat, om.precompose_ov(W["W_UV"], W["W_O"]))
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
