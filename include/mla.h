@@ -262,7 +262,50 @@ mla_status mla_out_proj_precomposed(const mla_dims* dims, int32_t B, const float
                                     const void* W_OV, void* out, void* ws, size_t ws_bytes,
                                     void* stream);
 
-/* Workspace bytes that suffice for every call above with these sizes
+/*
+ * Causal prefill: T new tokens per sequence attend over the cache, the step
+ * on the other side of the cache from decode. Two algorithms with the same
+ * inputs and outputs ("Understanding MLA", sections 5-6: the training form
+ * expands the latent and runs ordinary attention, the decode form keeps the
+ * latent and folds the up-projections into query and output; [KB] section 3
+ * sketch of the expanded form):
+ *   MLA_PREFILL_MATERIALIZED  K(i)_u = [W_UK(i) c_u ; k_R,u], V(i)_u = W_UV(i) c_u
+ *                             for every stored row, then per-head causal
+ *                             attention over d_h + d_R wide keys
+ *   MLA_PREFILL_ABSORBED      q_lat = W_UK(i)^T q_C per token, latent attention
+ *                             over the d_c + d_R wide rows (the decode kernel,
+ *                             one entry per token), o = W_UV(i) o_lat
+ * For token t of sequence b, at position p = seq_lens[b] - T + t (its own row
+ * and the earlier tokens' rows are already in the cache):
+ *   s(i,u) = scale * ([q_C ; q_R](b,t,i) . K(i)_u)    u = 0..p
+ *   o(b,t,i) = sum_u softmax_u(s(i,u)) V(i)_u,   lse(b,t,i) = ln sum_u exp s(i,u)
+ *   q      [B][T][H][d_h + d_R] storage dtype: per head [q_C ; q_R], q_R rotated
+ *          at the token's position
+ *   seq_lens [B] int32 device: rows of sequence b including its T tokens; a
+ *          token with p < 0 attends nothing (zeros, lse = -inf)
+ *   max_seq_len host upper bound of seq_lens
+ *   W_UK [H][d_h][d_c], W_UV [H][d_v][d_c]
+ *   o      [B][T][H][d_v] storage dtype out;  lse [B][T][H] float32 out, or NULL
+ *   ws     mla_prefill_workspace_bytes(dims, B, T, max_seq_len, cache, algo)
+ *          bytes. The materialised form expands every row the cache stores
+ *          (contiguous: B * capacity, paged: n_blocks * block_size) into it:
+ *          (d_h + d_v) * H elements per row.
+ * Errors: MLA_ERR_SHAPE for B, T <= 0, an unknown algo or max_seq_len above
+ * the cache; MLA_ERR_UNSUPPORTED if B * T exceeds 32768 (absorbed, V3
+ * geometry) or the cache has more than 2^31 - 1 rows (materialised).
+ */
+typedef enum { MLA_PREFILL_MATERIALIZED = 0, MLA_PREFILL_ABSORBED = 1 } mla_prefill_algo;
+
+mla_status mla_prefill_attn(const mla_dims* dims, int32_t B, int32_t T, const void* q,
+                            const mla_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                            const void* W_UK, const void* W_UV, int32_t algo, void* o, float* lse,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes mla_prefill_attn needs; 0 on bad arguments. */
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t B, int32_t T, int32_t max_seq_len,
+                                   const mla_cache* cache, int32_t algo);
+
+/* Workspace bytes that suffice for every call above except mla_prefill_attn, with these sizes
  * (num_splits as passed to mla_decode_attn, 0 = automatic). 0 on bad dims. */
 size_t mla_workspace_bytes(const mla_dims* dims, int32_t B, int32_t max_seq_len,
                            int32_t num_splits);

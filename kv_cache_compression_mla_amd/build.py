@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["attn_mfma.hip", "attn_generic.hip", "gemm.hip", "mla_api.cpp"]
+SOURCES = ["attn_mfma.hip", "attn_generic.hip", "attn_prefill.hip", "gemm.hip", "mla_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -62,7 +62,8 @@ __global__ __launch_bounds__(GT) void attn_generic_kernel(AttnArgs a) {
   const T* q = static_cast<const T*>(a.q) + (static_cast<long long>(b) * a.H + head) * D;
   const T* cache = static_cast<const T*>(a.cache);
   for (int k = tid; k < D; k += GT) qs[k] = Elem<T>::ld(q + k);
-  const int L = a.seq_lens[b];
+  const int L = virt_len(a.seq_lens, b, a.qpt);
+  const int bc = a.qpt == 1 ? b : b / a.qpt;   // the cached sequence it reads
   const int r0 = s_idx * a.chunk;
   const int r1 = min(r0 + a.chunk, L);
   const float sl2 = a.scale * 1.4426950408889634f;
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(GT) void attn_generic_kernel(AttnArgs a) {
     const int u = base + tid;
     float sc = -INFINITY;
     if (u < r1) {
-      const T* row = g_row_ptr(cache, a.block_table, a.capacity, a.block_size, a.max_blocks, D, b, u, a.indices,
+      const T* row = g_row_ptr(cache, a.block_table, a.capacity, a.block_size, a.max_blocks, D, bc, u, a.indices,
                                a.topk);
       float dot = 0.f;
       for (int k = 0; k < D; ++k) dot += qs[k] * Elem<T>::ld(row + k);
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(GT) void attn_generic_kernel(AttnArgs a) {
       if (c < a.d_c) {
         float x = acc[j] * alpha;
         for (int t = 0; t < nrow; ++t) {
-          const T* row = g_row_ptr(cache, a.block_table, a.capacity, a.block_size, a.max_blocks, D, b,
+          const T* row = g_row_ptr(cache, a.block_table, a.capacity, a.block_size, a.max_blocks, D, bc,
                                    base + t, a.indices, a.topk);
           x += ps[t] * Elem<T>::ld(row + c);
         }
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(GT) void attn_generic_kernel(AttnArgs a) {
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int head = blockIdx.x % a.H;
   const int b = blockIdx.x / a.H;
-  const int L = a.seq_lens[b];
+  const int L = virt_len(a.seq_lens, b, a.qpt);
   const int nv = min(a.splits, (L + a.chunk - 1) / a.chunk);
   float* o = a.o_lat + (static_cast<long long>(b) * a.H + head) * a.d_c;
   const long long base = static_cast<long long>(b) * a.splits * a.H + head;   // split 0

@@ -123,6 +123,7 @@ struct Params {
   int2* plan_seq;         // [B]: (first chunk, chunks) of each sequence
   const int32_t* indices; // gather modes: [B][topk] listed rows (seq_lens = counts)
   int topk;
+  int qpt;                // query tokens per cached sequence (causal prefill), 1 for decode
 };
 
 // ---- chunk plan ----
@@ -181,7 +182,7 @@ __device__ ChunkPlan plan_chunks(const Params& p, int* scratch, int* res) {
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int lane = tid;
-    for (int i = lane; i < p.B; i += 64) scratch[i] = p.seq_lens[i];
+    for (int i = lane; i < p.B; i += 64) scratch[i] = virt_len(p.seq_lens, i, p.qpt);
     // (LDS writes and reads below are by this wave only, in order)
     int target_rows = 0;   // balanced: the chunk size C
     if (p.splits == 0) {
@@ -444,6 +445,7 @@ void attn_mfma_kernel(Params p) {
   const ChunkPlan plan = plan_chunks(p, reinterpret_cast<int*>(smem), reinterpret_cast<int*>(smem + LM_OFF));
   if (plan.b < 0) return;             // no chunk for this workgroup
   const int b = plan.b;
+  const int bc = p.qpt == 1 ? b : b / p.qpt;   // the cached sequence it reads
   const int gi = blockIdx.x;          // chunk index (partials)
   const bool single = plan.n == 1;    // whole sequence here: final output
   if (tid == 0 && plan.r0 == 0) p.plan_seq[b] = int2{plan.start, plan.n};
@@ -501,7 +503,7 @@ void attn_mfma_kernel(Params p) {
   auto tile_r0 = [&](int t) { return row_begin + t * TILE; };
   auto tile_nv = [&](int t) { return min(TILE, row_end - tile_r0(t)); };
   auto copy_tile = [&](int t) {
-    const TileCopy c = plan_copy<PM>(p, b, tile_r0(t), row_end, w, lane);
+    const TileCopy c = plan_copy<PM>(p, bc, tile_r0(t), row_end, w, lane);
 #pragma unroll
     for (int k = 0; k < DMA_PER_WAVE; ++k)
       copy_part<PM>(c, k, smem_lds + lat_off(t), smem_lds + rope_off(t), w, lane_off);
@@ -667,7 +669,7 @@ void attn_mfma_kernel(Params p) {
       else wait_vmcnt<0>();
       block_barrier();
       const bool copy_next = t + 3 < ntiles;
-      const TileCopy c = plan_copy<PM>(p, b, tile_r0(copy_next ? t + 3 : t), row_end, w, lane);
+      const TileCopy c = plan_copy<PM>(p, bc, tile_r0(copy_next ? t + 3 : t), row_end, w, lane);
       const uint32_t lat3 = smem_lds + lat_off(t + 3), rope3 = smem_lds + rope_off(t + 3);
       Soft N;
       qk(t + 1, N.x, [&](int s) {
@@ -857,6 +859,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
   p.plan_seq = a.plan_seq;
   p.indices = a.indices;
   p.topk = a.topk;
+  p.qpt = a.qpt;
   const dim3 grid(a.grid);
   const int pm = a.indices ? (a.block_table ? GATHER_PAGED : GATHER_CONTIG)
                            : (!a.block_table ? CONTIG : (a.block_size >= 8 ? PAGED8 : PAGED_SMALL));

@@ -388,7 +388,7 @@ namespace {
 mla_status decode_attn_impl(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
                             const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_lat,
                             float* lse, void* ws, size_t ws_bytes, void* stream, const int32_t* indices,
-                            int32_t topk) {
+                            int32_t topk, int32_t qpt = 1) {
   MLA_TRY(check_dims(dims));
   if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
   if (max_seq_len < 0 || num_splits < 0) return fail(MLA_ERR_SHAPE, "negative max_seq_len or num_splits");
@@ -431,6 +431,7 @@ mla_status decode_attn_impl(const mla_dims* dims, int32_t B, const void* q, cons
   a.dtype = dims->dtype;
   a.indices = indices;
   a.topk = topk;
+  a.qpt = qpt;
   if (mfma) {
     // the device plans the chunks (balanced when num_splits is 0) and merges them
     const int s = mfma_splits(num_splits, max_seq_len);
@@ -461,9 +462,220 @@ mla_status decode_attn_impl(const mla_dims* dims, int32_t B, const void* q, cons
   return ok();
 }
 
+// ---- causal prefill (materialised or absorbed) ----
+
+bool prefill_mfma(const mla_dims* d, const mla_cache* c) {
+  return d->dtype == MLA_BF16 && d->d_h == 128 && d->d_R == 64 && d->d_v == 128 &&
+         (c->block_table == nullptr || c->block_size >= 8);
+}
+// Rows the cache stores (every one is expanded), and the transposed values'
+// row length and per-sequence column stride (contiguous cache: each
+// sequence's columns start on a multiple of 8).
+long long cache_store_rows(const mla_cache* c, int B) {
+  return c->block_table ? static_cast<long long>(c->n_blocks) * c->block_size
+                        : static_cast<long long>(B) * c->capacity;
+}
+long long vt_seq_stride(const mla_cache* c) { return c->block_table ? 0 : (c->capacity + 7LL) / 8 * 8; }
+long long vt_row_len(const mla_cache* c, int B) {
+  return c->block_table ? cache_store_rows(c, B) : static_cast<long long>(B) * vt_seq_stride(c);
+}
+
+// Partial bytes a gemm_store of this shape needs (none when it stores directly).
+size_t store_part_bytes(const GemmShape& s, int dtype, long long lda, long long sAg, bool a_f32, long long ldw,
+                        long long sWg, bool w_kn) {
+  alignas(16) static const char dummy[16] = {};
+  mla::GemmArgs g{dummy, lda, sAg, a_f32, dummy, ldw, sWg, w_kn, s.M, s.N, s.K, s.G, splits_for(s, dtype),
+                  nullptr, dtype};
+  g.out = const_cast<char*>(dummy);
+  return mla::gemm_direct(g) ? 0 : part_bytes(s, dtype);
+}
+
+struct PrefillPlan {
+  // materialised: expanded keys and transposed values, GEMM partials
+  size_t k_bytes = 0, vt_bytes = 0;
+  // absorbed: absorbed queries, latent outputs, attention workspace
+  size_t qa_bytes = 0, olat_bytes = 0, attn_bytes = 0;
+  size_t p_bytes = 0;
+  size_t total() const {
+    return align_up(k_bytes) + align_up(vt_bytes) + align_up(qa_bytes) + align_up(olat_bytes) +
+           align_up(attn_bytes) + align_up(p_bytes);
+  }
+};
+
+PrefillPlan prefill_plan(const mla_dims* d, int B, int T, int max_seq_len, const mla_cache* c, int algo) {
+  PrefillPlan pl;
+  const size_t es = elem_size(d->dtype);
+  const int H = d->H, D = d->d_c + d->d_R, DQ = d->d_h + d->d_R;
+  const bool f32 = d->dtype == MLA_FP32;
+  if (algo == MLA_PREFILL_MATERIALIZED) {
+    const long long rows = cache_store_rows(c, B);
+    pl.k_bytes = static_cast<size_t>(rows) * H * d->d_h * es;
+    pl.vt_bytes = static_cast<size_t>(H) * d->d_v * vt_row_len(c, B) * es;
+    const GemmShape sk{static_cast<int>(rows), H * d->d_h, d->d_c, 1};
+    const bool paged = c->block_table != nullptr;
+    const GemmShape sv{H * d->d_v, paged ? static_cast<int>(rows) : c->capacity, d->d_c, paged ? 1 : B};
+    pl.p_bytes = std::max(store_part_bytes(sk, d->dtype, D, 0, f32, d->d_c, 0, false),
+                          store_part_bytes(sv, d->dtype, d->d_c, 0, f32, D,
+                                           paged ? 0 : static_cast<long long>(c->capacity) * D, false));
+  } else {
+    const long long BT = static_cast<long long>(B) * T;
+    pl.qa_bytes = static_cast<size_t>(BT) * H * D * es;
+    pl.olat_bytes = static_cast<size_t>(BT) * H * d->d_c * sizeof(float);
+    pl.attn_bytes = ws_attn(d, static_cast<int>(BT), max_seq_len, 0);
+    const GemmShape sq{static_cast<int>(BT), d->d_c, d->d_h, H};
+    const GemmShape so{static_cast<int>(BT), d->d_v, d->d_c, H};
+    pl.p_bytes = std::max(store_part_bytes(sq, d->dtype, static_cast<long long>(H) * DQ, DQ, f32, d->d_c,
+                                           static_cast<long long>(d->d_h) * d->d_c, true),
+                          store_part_bytes(so, d->dtype, static_cast<long long>(H) * d->d_c, d->d_c, true, d->d_c,
+                                           static_cast<long long>(d->d_v) * d->d_c, false));
+  }
+  return pl;
+}
+
+constexpr long long kMaxPrefillRows = 0x7fffffffLL;
+
+mla_status check_prefill_sizes(const mla_dims* d, int B, int T, int max_seq_len, const mla_cache* c, int algo) {
+  if (B <= 0 || T <= 0) return fail(MLA_ERR_SHAPE, "prefill: B and T must be positive");
+  if (max_seq_len < 0) return fail(MLA_ERR_SHAPE, "prefill: negative max_seq_len");
+  if (algo != MLA_PREFILL_MATERIALIZED && algo != MLA_PREFILL_ABSORBED)
+    return fail(MLA_ERR_SHAPE, "prefill: unknown algorithm %d", algo);
+  MLA_TRY(check_cache(d, c));
+  if (!c->block_table && max_seq_len > c->capacity)
+    return fail(MLA_ERR_SHAPE, "max_seq_len %d exceeds capacity %d", max_seq_len, c->capacity);
+  if (c->block_table && static_cast<long long>(max_seq_len) > static_cast<long long>(c->max_blocks) * c->block_size)
+    return fail(MLA_ERR_SHAPE, "max_seq_len exceeds max_blocks * block_size");
+  if (algo == MLA_PREFILL_MATERIALIZED) {
+    if (cache_store_rows(c, B) > kMaxPrefillRows || static_cast<long long>(d->H) * d->d_v > kMaxPrefillRows)
+      return fail(MLA_ERR_UNSUPPORTED, "prefill: cache too large to expand in one product");
+    if (!prefill_mfma(d, c) && d->d_v > 1024) return fail(MLA_ERR_UNSUPPORTED, "prefill: d_v above 1024");
+  } else {
+    const long long BT = static_cast<long long>(B) * T;
+    if (mfma_attn(d) && BT > kMaxMfmaBatch)
+      return fail(MLA_ERR_UNSUPPORTED, "prefill (absorbed): B * T above %d", kMaxMfmaBatch);
+    if (BT > kMaxPrefillRows) return fail(MLA_ERR_UNSUPPORTED, "prefill: B * T too large");
+  }
+  return MLA_OK;
+}
+
+mla_status prefill_materialized(const mla_dims* d, int B, int T, const void* q, const mla_cache* c,
+                                const int32_t* seq_lens, const void* W_UK, const void* W_UV, void* o, float* lse,
+                                const PrefillPlan& pl, char* w, hipStream_t st) {
+  const int dt = d->dtype;
+  const bool f32 = dt == MLA_FP32;
+  const int H = d->H, D = d->d_c + d->d_R;
+  void* Kx = w;
+  w += align_up(pl.k_bytes);
+  void* Vt = w;
+  w += align_up(pl.vt_bytes);
+  float* P = reinterpret_cast<float*>(w);
+  const long long rows = cache_store_rows(c, B);
+  const bool paged = c->block_table != nullptr;
+  const long long vt_ld = vt_row_len(c, B), vt_seq = vt_seq_stride(c);
+  // K[row][i*d_h + k] = (W_UK(i) c_row)[k] for every stored row
+  {
+    const GemmShape s{static_cast<int>(rows), H * d->d_h, d->d_c, 1};
+    MLA_TRY(gemm_store(c->data, D, 0, f32, W_UK, d->d_c, 0, false, s, dt, P, Kx, static_cast<long long>(H) * d->d_h,
+                       0, st));
+  }
+  // Vt[i*d_v + j][col] = (W_UV(i) c_row)[j]: W_UV times the rows, per sequence
+  // (contiguous) or over the whole pool (paged)
+  {
+    const GemmShape s{H * d->d_v, paged ? static_cast<int>(rows) : c->capacity, d->d_c, paged ? 1 : B};
+    MLA_TRY(gemm_store(W_UV, d->d_c, 0, f32, c->data, D, paged ? 0 : static_cast<long long>(c->capacity) * D, false,
+                       s, dt, P, Vt, vt_ld, paged ? 0 : vt_seq, st));
+  }
+  mla::PrefillArgs a{};
+  a.q = q;
+  a.K = Kx;
+  a.Vt = Vt;
+  a.vt_ld = vt_ld;
+  a.vt_seq = vt_seq;
+  a.cache = c->data;
+  a.block_table = c->block_table;
+  a.capacity = c->capacity;
+  a.block_size = c->block_size;
+  a.max_blocks = c->max_blocks;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.d_h = d->d_h;
+  a.d_v = d->d_v;
+  a.d_c = d->d_c;
+  a.d_R = d->d_R;
+  a.scale = softmax_scale(d);
+  a.o = o;
+  a.lse = lse;
+  a.dtype = dt;
+  if (prefill_mfma(d, c)) return hip_status(mla::launch_prefill_mfma(a, st), "prefill launch");
+  return hip_status(mla::launch_prefill_generic(a, st), "prefill launch");
+}
+
+mla_status prefill_absorbed(const mla_dims* d, int B, int T, const void* q, const mla_cache* c,
+                            const int32_t* seq_lens, int max_seq_len, const void* W_UK, const void* W_UV, void* o,
+                            float* lse, const PrefillPlan& pl, char* w, hipStream_t st) {
+  const int dt = d->dtype;
+  const size_t es = elem_size(dt);
+  const bool f32 = dt == MLA_FP32;
+  const int H = d->H, D = d->d_c + d->d_R, DQ = d->d_h + d->d_R;
+  const int BT = B * T;
+  void* qa = w;
+  w += align_up(pl.qa_bytes);
+  float* olat = reinterpret_cast<float*>(w);
+  w += align_up(pl.olat_bytes);
+  void* aw = w;
+  w += align_up(pl.attn_bytes);
+  float* P = reinterpret_cast<float*>(w);
+  // q_lat(t, i) = W_UK(i)^T q_C(t, i) into qa[t][i][0:d_c]
+  {
+    const GemmShape s{BT, d->d_c, d->d_h, H};
+    MLA_TRY(gemm_store(q, static_cast<long long>(H) * DQ, DQ, f32, W_UK, d->d_c, static_cast<long long>(d->d_h) * d->d_c,
+                       true, s, dt, P, qa, static_cast<long long>(H) * D, D, st));
+  }
+  // q_R(t, i) beside it
+  MLA_TRY(hip_status(hipMemcpy2DAsync(static_cast<char*>(qa) + static_cast<size_t>(d->d_c) * es, D * es,
+                                      static_cast<const char*>(q) + static_cast<size_t>(d->d_h) * es, DQ * es,
+                                      static_cast<size_t>(d->d_R) * es, static_cast<size_t>(BT) * H,
+                                      hipMemcpyDeviceToDevice, st),
+                     "rotary query copy"));
+  // token t of sequence b attends rows 0 .. seq_lens[b] - T + t
+  MLA_TRY(decode_attn_impl(d, BT, qa, c, seq_lens, max_seq_len, 0, olat, lse, aw, pl.attn_bytes, st, nullptr, 0, T));
+  // o(t, i) = W_UV(i) o_lat(t, i)
+  const GemmShape s{BT, d->d_v, d->d_c, H};
+  return gemm_store(olat, static_cast<long long>(H) * d->d_c, d->d_c, true, W_UV, d->d_c,
+                    static_cast<long long>(d->d_v) * d->d_c, false, s, dt, P, o, static_cast<long long>(H) * d->d_v,
+                    d->d_v, st);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t B, int32_t T, int32_t max_seq_len,
+                                   const mla_cache* cache, int32_t algo) {
+  if (check_dims(dims) != MLA_OK || !cache) return 0;
+  if (check_prefill_sizes(dims, B, T, max_seq_len, cache, algo) != MLA_OK) return 0;
+  return prefill_plan(dims, B, T, max_seq_len, cache, algo).total();
+}
+
+mla_status mla_prefill_attn(const mla_dims* dims, int32_t B, int32_t T, const void* q, const mla_cache* cache,
+                            const int32_t* seq_lens, int32_t max_seq_len, const void* W_UK, const void* W_UV,
+                            int32_t algo, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (!q || !cache || !seq_lens || !W_UK || !W_UV || !o || !ws) return fail(MLA_ERR_NULL, "prefill: NULL pointer");
+  MLA_TRY(check_prefill_sizes(dims, B, T, max_seq_len, cache, algo));
+  for (const void* p : {q, static_cast<const void*>(seq_lens), W_UK, W_UV, static_cast<const void*>(o),
+                        static_cast<const void*>(ws)})
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "prefill: pointer not 16-byte aligned");
+  if (lse && !aligned16(lse)) return fail(MLA_ERR_ALIGN, "prefill: lse not 16-byte aligned");
+  const PrefillPlan pl = prefill_plan(dims, B, T, max_seq_len, cache, algo);
+  if (ws_bytes < pl.total()) return fail(MLA_ERR_WORKSPACE, "prefill needs %zu bytes", pl.total());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (algo == MLA_PREFILL_MATERIALIZED)
+    return prefill_materialized(dims, B, T, q, cache, seq_lens, W_UK, W_UV, o, lse, pl, w, st);
+  return prefill_absorbed(dims, B, T, q, cache, seq_lens, max_seq_len, W_UK, W_UV, o, lse, pl, w, st);
+}
 
 mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
                            const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_lat,

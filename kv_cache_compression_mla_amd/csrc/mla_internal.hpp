@@ -135,7 +135,43 @@ struct AttnArgs {
   // (seq_lens then holds the entry counts)
   const int32_t* indices = nullptr;
   int topk = 0;
+  // causal prefill in the absorbed form: B counts query tokens, qpt of them
+  // per cached sequence; entry b attends the first virt_len(...) rows of
+  // sequence b / qpt
+  int qpt = 1;
 };
+
+// Rows attended by entry b: seq_lens[b] for decode (qpt = 1); with qpt query
+// tokens per sequence, token t = b % qpt of sequence b / qpt sits at position
+// seq_lens - qpt + t and attends the rows up to and including it.
+__device__ __forceinline__ int virt_len(const int32_t* seq_lens, int b, int qpt) {
+  if (qpt == 1) return seq_lens[b];
+  return max(0, seq_lens[b / qpt] - (qpt - 1 - b % qpt));
+}
+// Causal prefill attention in the materialised form: keys and values expanded
+// per head from the cached latents, T query tokens per sequence, token t at
+// position seq_lens[b] - T + t attending rows 0..that position.
+struct PrefillArgs {
+  const void* q;            // [B][T][H][d_h + d_R]: per head [q_C ; q_R]
+  const void* K;            // [cache storage rows][H][d_h]: expanded keys (nope part)
+  const void* Vt;           // [H][d_v][vt_ld]: expanded values, transposed
+  long long vt_ld;          // row length of Vt
+  long long vt_seq;         // contiguous cache: Vt column of row u of sequence b is b*vt_seq + u
+  const void* cache;        // latent rows [c ; k_R]; the rotary keys are read here
+  const int32_t* block_table;
+  long long capacity;
+  int block_size, max_blocks;
+  const int32_t* seq_lens;  // rows per sequence, the T tokens' own rows included
+  int B, T, H, d_h, d_v, d_c, d_R;
+  float scale;
+  void* o;                  // [B][T][H][d_v] storage dtype
+  float* lse;               // [B][T][H] or NULL
+  int dtype;
+};
+// MFMA kernel: bf16, d_h = d_v = 128, d_R = 64, contiguous or block_size >= 8.
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t stream);
+
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);

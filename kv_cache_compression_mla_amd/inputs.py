@@ -33,7 +33,7 @@ BF16_NAN = np.uint16(0x7FC0)
 # Order in which child random streams are spawned from the seed. Fixed so that
 # every consumer draws identical values.
 _STREAMS = ("W_DKV", "W_KR", "W_DQ", "W_UQ", "W_QR", "W_UK", "W_UV", "W_O",
-            "h_t", "history", "ctx", "pages", "gamma", "q", "topk")
+            "h_t", "history", "ctx", "pages", "gamma", "q", "topk", "prefill_q")
 
 
 @dataclass(frozen=True)
@@ -288,3 +288,10 @@ def make_query(cfg: MLAConfig, q_std: float = 0.5) -> np.ndarray:
     exercising the attention call on its own (default std gives scores of
     about the spread a full V3-shaped step produces)."""
     return _draw(_rngs(cfg.seed)["q"], (cfg.B, cfg.H, cfg.D), q_std, cfg.dtype)
+
+
+def make_prefill_query(cfg: MLAConfig, T: int, q_std: float = 1.0) -> np.ndarray:
+    """A seeded per-head query [B][T][H][d_h + d_R] ([q_C ; q_R] per head) in the
+    storage dtype for T prefill tokens per sequence (std 1 gives scores of a
+    spread similar to the decode workloads against the history rows)."""
+    return _draw(_rngs(cfg.seed)["prefill_q"], (cfg.B, T, cfg.H, cfg.d_h + cfg.d_R), q_std, cfg.dtype)

@@ -59,6 +59,12 @@ _SIGS = {
                                  + [ctypes.c_size_t, ctypes.c_void_p]),
     "mla_out_proj_precomposed": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32] + [ctypes.c_void_p] * 4
                                  + [ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_prefill_attn": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.POINTER(MLACache), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.POINTER(MLACache), ctypes.c_int32]),
     "mla_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32]),
     "mla_decode_num_splits": (ctypes.c_int32, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
@@ -221,3 +227,22 @@ def mla_out_proj_precomposed(dims, o_lat, W_OV, out, ws, stream=None):
     _check(lib().mla_out_proj_precomposed(
         ctypes.byref(dims), B, _ptr(o_lat, torch.float32, "o_lat"), _ptr(W_OV, dt, "W_OV"), _ptr(out, dt, "out"),
         _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)), "mla_out_proj_precomposed")
+
+
+PREFILL_MATERIALIZED, PREFILL_ABSORBED = 0, 1
+
+
+def prefill_workspace_bytes(dims: MLADims, B: int, T: int, max_seq_len: int, cache: MLACache, algo: int) -> int:
+    return lib().mla_prefill_workspace_bytes(ctypes.byref(dims), B, T, max_seq_len, ctypes.byref(cache), algo)
+
+
+def mla_prefill_attn(dims, q, cache: MLACache, seq_lens, max_seq_len: int, W_UK, W_UV, algo: int, o, lse=None,
+                     ws=None, stream=None):
+    """q [B][T][H][d_h + d_R] -> o [B][T][H][d_v] (+ lse [B][T][H]); causal over each sequence's rows."""
+    dt = dims.torch_dtype
+    B, T = int(q.shape[0]), int(q.shape[1])
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().mla_prefill_attn(
+        ctypes.byref(dims), B, T, _ptr(q, dt, "q"), ctypes.byref(cache), _ptr(seq_lens, torch.int32, "seq_lens"),
+        int(max_seq_len), _ptr(W_UK, dt, "W_UK"), _ptr(W_UV, dt, "W_UV"), int(algo), _ptr(o, dt, "o"),
+        _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"), wsz, _stream(stream)), "mla_prefill_attn")

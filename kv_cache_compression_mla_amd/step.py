@@ -120,3 +120,38 @@ class DeviceStep:
         bs = self.cfg.block_size
         blk = int(self.inp.block_table[b, u // bs])
         return self.host(self.cache[blk, u % bs])
+
+
+class DevicePrefill:
+    """Causal prefill of the newest T tokens of every sequence: the cache holds
+    ctx_b rows per sequence (the T tokens' own rows among them), q is the
+    seeded per-head query [B][T][H][d_h + d_R]."""
+
+    def __init__(self, inp: MLAInputs, T: int, device="cuda", q_std: float = 1.0):
+        from .inputs import make_prefill_query
+        cfg = inp.cfg
+        self.cfg, self.inp, self.T = cfg, inp, T
+        dt = cfg.dtype
+        self.W_UK = to_device(inp.weights["W_UK"], dt, device)
+        self.W_UV = to_device(inp.weights["W_UV"], dt, device)
+        self.cache = to_device(inp.cache, dt, device)
+        self.block_table = (None if inp.block_table is None
+                            else torch.from_numpy(inp.block_table).to(device))
+        self.seq_lens_host = inp.ctx.astype(np.int32)
+        self.seq_lens = torch.from_numpy(self.seq_lens_host).to(device)
+        self.max_seq_len = int(self.seq_lens_host.max())
+        self.dims = mla.make_dims(cfg.d, cfg.H, cfg.d_h, cfg.d_v, cfg.d_c, cfg.d_R, cfg.d_cq, dt,
+                                  softmax_scale=cfg.scale, rope_theta=cfg.theta)
+        self.cdesc = mla.make_cache(self.cache, self.block_table)
+        self.q_host = make_prefill_query(cfg, T, q_std)
+        self.q = to_device(self.q_host, dt, device)
+        tdt = self.dims.torch_dtype
+        self.o = torch.empty(cfg.B, T, cfg.H, cfg.d_v, dtype=tdt, device=device)
+        self.lse = torch.empty(cfg.B, T, cfg.H, dtype=torch.float32, device=device)
+        ws = max(mla.prefill_workspace_bytes(self.dims, cfg.B, T, self.max_seq_len, self.cdesc, a)
+                 for a in (mla.PREFILL_MATERIALIZED, mla.PREFILL_ABSORBED))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=device)
+
+    def run(self, algo: int):
+        mla.mla_prefill_attn(self.dims, self.q, self.cdesc, self.seq_lens, self.max_seq_len, self.W_UK, self.W_UV,
+                             algo, self.o, self.lse, self.ws)

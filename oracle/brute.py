@@ -81,3 +81,45 @@ def brute_step(h, prior_rows, W, pos, theta, scale, round_fn):
     flat = [x for o in o_all for x in o]
     out = _matvec(W["W_O"], flat)
     return new_row, o_all, out
+
+
+def brute_prefill(qC, qR, rows, T, W_UK, W_UV, scale):
+    """Causal prefill of the last T tokens of a sequence with rows [L][d_c + d_R]:
+    token t at position L - T + t attends rows 0..L - T + t with keys
+    [W_UK(i) c_u ; kR_u] and values W_UV(i) c_u, everything in loops.
+    qC [T][H][d_h], qR [T][H][d_R] nested lists -> o [T][H][d_v]."""
+    L = len(rows)
+    H = len(W_UK)
+    d_h = len(W_UK[0])
+    d_c = len(W_UK[0][0])
+    d_v = len(W_UV[0])
+    out = []
+    for t in range(T):
+        p = L - T + t
+        per_head = []
+        for i in range(H):
+            if p < 0:
+                per_head.append([0.0] * d_v)
+                continue
+            scores = []
+            for u in range(p + 1):
+                c = rows[u][:d_c]
+                kr = rows[u][d_c:]
+                kn = _matvec(W_UK[i], c)
+                dot = 0.0
+                for k in range(d_h):
+                    dot += float(qC[t][i][k]) * kn[k]
+                for k in range(len(kr)):
+                    dot += float(qR[t][i][k]) * float(kr[k])
+                scores.append(dot * scale)
+            mx = max(scores)
+            ws = [math.exp(x - mx) for x in scores]
+            tot = sum(ws)
+            o = [0.0] * d_v
+            for u in range(p + 1):
+                v = _matvec(W_UV[i], rows[u][:d_c])
+                for j in range(d_v):
+                    o[j] += ws[u] / tot * v[j]
+            per_head.append(o)
+        out.append(per_head)
+    return out

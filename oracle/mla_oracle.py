@@ -227,6 +227,86 @@ def expand_out(o_lat, W_UV) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Causal prefill (several query tokens per sequence)
+# --------------------------------------------------------------------------
+
+def prefill_positions(L: int, T: int) -> np.ndarray:
+    """Positions of the T newest tokens of a sequence whose L rows include
+    them: token t sits at L - T + t (negative when L < T: such a token has no
+    row to attend)."""
+    return np.arange(T, dtype=np.int64) + (L - T)
+
+
+def prefill_attend(qC, qR, rows, pos, W_UK, W_UV, scale: float, head_block: int = 16):
+    """Causal attention of query tokens at positions pos over one sequence's
+    rows, the training / materialised way (the definition).
+
+    Every head's keys and values are rebuilt from each cached latent,
+    K(i)_u = [W_UK(i) c_u ; kR_u] and V(i)_u = W_UV(i) c_u ("Understanding
+    MLA", phases B and D and sections 5-6; [KB] section 3 sketch expands the
+    latent and runs ordinary attention over [B, H, T, T] scores). Token n
+    attends rows u <= pos[n]: o(n, i) = softmax_u(scale * q(n, i) . K(i)_u)
+    V(i), lse(n, i) = ln sum_u exp(...). A token with pos < 0 attends nothing:
+    zeros and lse = -inf.
+    qC [n][H][d_h], qR [n][H][d_R], rows [L][d_c + d_R] -> (o [n][H][d_v], lse [n][H]).
+    """
+    qC = np.asarray(qC, dtype=np.float64)
+    qR = np.asarray(qR, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    W_UK = np.asarray(W_UK, dtype=np.float64)
+    W_UV = np.asarray(W_UV, dtype=np.float64)
+    H, d_h, d_c = W_UK.shape
+    d_v = W_UV.shape[1]
+    n = qC.shape[0]
+    o = np.zeros((n, H, d_v))
+    lse = np.full((n, H), -np.inf)
+    if n == 0 or pos.max() < 0:
+        return o, lse
+    used = rows[:int(pos.max()) + 1]
+    c, kR = used[:, :d_c], used[:, d_c:]
+    keys = np.arange(used.shape[0])
+    mask = keys[None, :] > pos[:, None]                                  # [n][L']
+    live = pos >= 0
+    for i0 in range(0, H, head_block):
+        i1 = min(H, i0 + head_block)
+        nh = i1 - i0
+        Kn = (c @ W_UK[i0:i1].reshape(nh * d_h, d_c).T).reshape(-1, nh, d_h)
+        V = (c @ W_UV[i0:i1].reshape(nh * d_v, d_c).T).reshape(-1, nh, d_v)
+        for t in range(nh):
+            i = i0 + t
+            K = np.concatenate([Kn[:, t, :], kR], axis=1)                # [L'][d_h + d_R]
+            q = np.concatenate([qC[:, i, :], qR[:, i, :]], axis=1)       # [n][d_h + d_R]
+            s = (q @ K.T) * scale
+            s[mask] = -np.inf
+            m = np.where(live, s.max(axis=1), 0.0)
+            p = np.exp(s - m[:, None])
+            l = p.sum(axis=1)
+            o[live, i] = (p[live] @ V[:, t, :]) / l[live, None]
+            lse[live, i] = m[live] + np.log(l[live])
+    return o, lse
+
+
+def prefill_attend_absorbed(qC, qR, rows, pos, W_UK, W_UV, scale: float):
+    """The same causal prefill in the absorbed form: per token q_lat(i) =
+    W_UK(i)^T q_C(i), latent attention over rows 0..pos ([DONG] section 4),
+    then o(i) = W_UV(i) o_lat(i)."""
+    rows = np.asarray(rows, dtype=np.float64)
+    H = np.asarray(W_UK).shape[0]
+    d_v = np.asarray(W_UV).shape[1]
+    n = len(pos)
+    o = np.zeros((n, H, d_v))
+    lse = np.full((n, H), -np.inf)
+    for k in range(n):
+        if pos[k] < 0:
+            continue
+        q_lat = absorb_q(qC[k], W_UK)
+        o_lat, lse[k] = attend_absorbed(q_lat, np.asarray(qR[k], dtype=np.float64), rows[:int(pos[k]) + 1], scale)
+        o[k] = expand_out(o_lat, W_UV)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
 # Precomposed weights
 # --------------------------------------------------------------------------
 

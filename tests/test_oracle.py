@@ -508,3 +508,68 @@ def test_precomposed_query_and_output_equal_the_two_step_forms_at_v3_width():
     ref = om.out_proj(om.expand_out(o_lat, W["W_UV"]), W["W_O"])
     got = om.out_proj_precomposed(o_lat, om.precompose_ov(W["W_UV"], W["W_O"]))
     assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+# --------------------------------------------------------------------------
+# Causal prefill
+# --------------------------------------------------------------------------
+
+def _prefill_case(cfg, T, b=0):
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    L = int(inp.ctx[b])
+    q = gen.to_f64(gen.make_prefill_query(cfg, T), cfg.dtype)[b]
+    rows = gen.to_f64(inp.rows(b, L), cfg.dtype)
+    return W, q[..., :cfg.d_h], q[..., cfg.d_h:], rows, L
+
+
+@pytest.mark.parametrize("L,T", [(9, 4), (3, 5), (1, 1)])
+def test_prefill_matches_brute_force(L, T):
+    """The materialised causal prefill against explicit loops (tiny geometry),
+    including more tokens than rows (the early tokens attend nothing)."""
+    cfg = gen.CONFIGS["tiny_fp32"].with_(ctx=(L,))
+    W, qC, qR, rows, L = _prefill_case(cfg, T)
+    o, lse = om.prefill_attend(qC, qR, rows, om.prefill_positions(L, T), W["W_UK"], W["W_UV"], cfg.scale)
+    ref = np.array(brute.brute_prefill(qC.tolist(), qR.tolist(), rows.tolist(), T, W["W_UK"].tolist(),
+                                       W["W_UV"].tolist(), cfg.scale))
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-15)
+    dead = om.prefill_positions(L, T) < 0
+    assert np.all(np.isneginf(lse[dead])) and not o[dead].any()
+    assert np.isfinite(lse[~dead]).all()
+
+
+def test_prefill_absorbed_equals_materialised():
+    """Both factorisations of the causal prefill agree to 1e-12 in float64 at the
+    V3 widths (the absorption identity per token, "Understanding MLA" section 4)."""
+    cfg = small_v3(B=1, ctx=(50,), seed=6)
+    W, qC, qR, rows, L = _prefill_case(cfg, 7)
+    pos = om.prefill_positions(L, 7)
+    o, lse = om.prefill_attend(qC, qR, rows, pos, W["W_UK"], W["W_UV"], cfg.scale)
+    oa, la = om.prefill_attend_absorbed(qC, qR, rows, pos, W["W_UK"], W["W_UV"], cfg.scale)
+    assert np.abs(o - oa).max() <= 1e-12 * np.abs(o).max()
+    np.testing.assert_allclose(la, lse, rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_single_token_is_the_decode_attention():
+    """T = 1: the one token sits at the last row and attends everything, as the
+    decode step's (unabsorbed) attention does."""
+    cfg = small_v3(B=1, ctx=(40,), seed=8)
+    W, qC, qR, rows, L = _prefill_case(cfg, 1)
+    o, _ = om.prefill_attend(qC, qR, rows, om.prefill_positions(L, 1), W["W_UK"], W["W_UV"], cfg.scale)
+    ref = om.attend_unabsorbed(qC[0], qR[0], rows, W["W_UK"], W["W_UV"], cfg.scale)
+    np.testing.assert_allclose(o[0], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_is_causal():
+    """A token's output does not depend on rows after its position: replacing
+    them leaves it bit for bit unchanged, while the last token's output moves."""
+    cfg = gen.CONFIGS["tiny_fp32"].with_(ctx=(20,))
+    W, qC, qR, rows, L = _prefill_case(cfg, 6)
+    pos = om.prefill_positions(L, 6)
+    o, lse = om.prefill_attend(qC, qR, rows, pos, W["W_UK"], W["W_UV"], cfg.scale)
+    rows2 = rows.copy()
+    rows2[int(pos[3]) + 1:] = np.random.default_rng(0).standard_normal(rows2[int(pos[3]) + 1:].shape)
+    o2, lse2 = om.prefill_attend(qC, qR, rows2, pos, W["W_UK"], W["W_UV"], cfg.scale)
+    np.testing.assert_array_equal(o2[:4], o[:4])
+    np.testing.assert_array_equal(lse2[:4], lse[:4])
+    assert np.abs(o2[5] - o[5]).max() > 1e-6
