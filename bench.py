@@ -97,6 +97,63 @@ def cpu_baseline(inp, budget_s, topk=None):
                       f"algorithmic attention FLOPs as the GPU line"}
 
 
+def prefill_work(cfg, seq_lens, T, rows_stored):
+    """Algorithmic FLOPs of causal prefill of the newest T tokens, per algorithm.
+    Attended rows: token t of a sequence of L rows sees L - T + t + 1 of them.
+    Materialised: expanding every stored row, 2 d_c H (d_h + d_v) per row, then
+    2 H (d_h + d_R + d_v) per attended row. Absorbed: W_UK^T per token
+    (2 H d_h d_c), 2 H (2 d_c + d_R) per attended row, W_UV per token (2 H d_c d_v)."""
+    att = 0
+    for L in seq_lens:
+        L = int(L)
+        att += sum(max(0, L - T + t + 1) for t in range(T))
+    H = cfg.H
+    mat = 2 * rows_stored * cfg.d_c * H * (cfg.d_h + cfg.d_v) + 2 * H * (cfg.d_h + cfg.d_R + cfg.d_v) * att
+    ntok = len(seq_lens) * T
+    absb = (2 * ntok * H * cfg.d_h * cfg.d_c + 2 * H * (2 * cfg.d_c + cfg.d_R) * att
+            + 2 * ntok * H * cfg.d_c * cfg.d_v)
+    return att, mat, absb
+
+
+def prefill_sweep(Ts, steps, warmup):
+    """Causal prefill of the newest T tokens of 4 sequences of 4096 cached rows:
+    the materialised form (expand every row's per-head keys and values, then
+    per-head causal attention) against the absorbed form (latent attention,
+    one entry per token), same inputs and outputs, timed with HIP events on
+    the stream the library launches on."""
+    import numpy as np
+    import torch
+    from kv_cache_compression_mla_amd import inputs as gen
+    from kv_cache_compression_mla_amd import mla
+    from kv_cache_compression_mla_amd.step import DevicePrefill
+    cfg = gen.CONFIGS["v3_b4_ctx4k_prefill"]
+    inp = gen.make_inputs(cfg)
+    stream = torch.cuda.current_stream()
+    for T in Ts:
+        pf = DevicePrefill(inp, T)
+        rows_stored = cfg.B * inp.cache.shape[1]
+        att, f_mat, f_abs = prefill_work(cfg, pf.seq_lens_host, T, rows_stored)
+        res = {"workload": cfg.name, "T": T, "tokens": cfg.B * T, "rows_attended": att}
+        for name, algo, flops in (("materialised", mla.PREFILL_MATERIALIZED, f_mat),
+                                  ("absorbed", mla.PREFILL_ABSORBED, f_abs)):
+            for _ in range(warmup):
+                pf.run(algo)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            torch.cuda.synchronize()
+            for a, b in ev:
+                a.record(stream)
+                pf.run(algo)
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            res[name] = {"ms": round(ms, 4), "GFLOP": round(flops / 1e9, 2),
+                         "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+        res["faster"] = min(("materialised", "absorbed"), key=lambda k: res[k]["ms"])
+        print(json.dumps(res), flush=True)
+        del pf
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +163,9 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-sweep", default="",
+                    help="comma-separated token counts T: time causal prefill of the newest T tokens of "
+                         "v3_b4_ctx4k_prefill, materialised against absorbed (one JSON line per T)")
     ap.add_argument("--precomposed", action="store_true",
                     help="query and output sides with composed weights W_QK, W_OV (formed before timing)")
     args = ap.parse_args()
@@ -124,6 +184,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.prefill_sweep:
+        prefill_sweep([int(x) for x in args.prefill_sweep.split(",")], args.steps, args.warmup)
+        return
     cfg = gen.CONFIGS[args.workload]
     t0 = time.perf_counter()
     inp = gen.make_inputs(cfg)

@@ -92,6 +92,8 @@ CONFIGS = {
     "v3_b64_ctx8k_norm": MLAConfig(name="v3_b64_ctx8k_norm", B=64, ctx=(8192,) * 64, gamma=True, **_V3),
     # sparse attention over a top-2048 list per sequence at the headline size
     "v3_b64_ctx8k_topk2048": MLAConfig(name="v3_b64_ctx8k_topk2048", B=64, ctx=(8192,) * 64, topk=2048, **_V3),
+    # causal prefill: the newest T tokens of 4 sequences of 4096 cached rows
+    "v3_b4_ctx4k_prefill": MLAConfig(name="v3_b4_ctx4k_prefill", B=4, ctx=(4096,) * 4, **_V3),
 }
 CONFIG_ORDER = list(CONFIGS)
 

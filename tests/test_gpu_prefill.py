@@ -1,0 +1,142 @@
+"""GPU parity of the causal prefill (materialised and absorbed) against the oracle.
+
+Both algorithms take the same seeded per-head query and the same cache and
+must give the oracle's per-head outputs and log-sum-exp: 1e-4 of the largest
+reference value for fp32 storage, 1e-2 for bf16. Tokens with no row to
+attend (more tokens than rows) must give zeros and lse = -inf exactly.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_mla_amd import inputs as gen
+from kv_cache_compression_mla_amd import mla
+from kv_cache_compression_mla_amd.step import DevicePrefill
+from oracle import mla_oracle as om
+from _common import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = {"materialised": mla.PREFILL_MATERIALIZED, "absorbed": mla.PREFILL_ABSORBED}
+V3 = gen.CONFIGS["v3_b1_ctx4k"]
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def weights64(inp):
+    dt = inp.cfg.dtype
+    return {k: (None if v is None else gen.to_f64(v, dt)) for k, v in inp.weights.items()}
+
+
+def oracle_tokens(pf, W, b, tokens):
+    cfg = pf.cfg
+    L = int(pf.seq_lens_host[b])
+    q = gen.to_f64(pf.q_host[b, tokens], cfg.dtype)
+    pos = om.prefill_positions(L, pf.T)[tokens]
+    rows = gen.to_f64(pf.inp.rows(b, L), cfg.dtype)
+    return om.prefill_attend(q[..., :cfg.d_h], q[..., cfg.d_h:], rows, pos, W["W_UK"], W["W_UV"], cfg.scale)
+
+
+def check(pf, W, label, seqs=None, tokens=None):
+    cfg = pf.cfg
+    t = 1e-4 if cfg.dtype == "fp32" else 1e-2
+    o = pf.o.detach().to(torch.float64).cpu().numpy()
+    lse = pf.lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all(), "non-finite output"
+    for b in (range(cfg.B) if seqs is None else seqs):
+        toks = np.arange(pf.T) if tokens is None else np.asarray(tokens)
+        ro, rl = oracle_tokens(pf, W, b, toks)
+        dead = np.isneginf(rl)
+        assert np.array_equal(np.isneginf(lse[b, toks]), dead), (label, b, "lse -inf pattern")
+        assert not o[b, toks][dead].any(), (label, b, "dead tokens must be zero")
+        e_o = np.abs(o[b, toks] - ro).max() / max(np.abs(ro).max(), 1e-30)
+        live = ~dead
+        e_l = (np.abs(lse[b, toks][live] - rl[live]).max() / max(np.abs(rl[live]).max(), 1.0)) if live.any() else 0.0
+        say(f"{label} b={b} L={int(pf.seq_lens_host[b])} tokens={len(toks)} o {e_o:.2e} lse {e_l:.2e}")
+        assert e_o <= t and e_l <= t, (label, b, e_o, e_l)
+
+
+def run(pf, algo_name):
+    pf.o.fill_(float("nan"))
+    pf.lse.fill_(float("nan"))
+    pf.run(ALGOS[algo_name])
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_prefill_tiny_fp32(algo):
+    cfg = gen.CONFIGS["tiny_fp32"].with_(ctx=(64,))
+    inp = make_inputs(cfg)
+    pf = DevicePrefill(inp, 5)
+    say(f"prefill tiny_fp32 {algo} T=5")
+    run(pf, algo)
+    check(pf, weights64(inp), f"tiny {algo}")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_prefill_v3_small_ragged(algo, paged):
+    """Three sequences of 45, 300 and 7 rows, 40 tokens each: a partial query
+    tile, masked diagonal tiles, and a sequence with fewer rows than tokens."""
+    cfg = V3.with_(name="v3_prefill_small", B=3, ctx=(45, 300, 7), paged=paged, block_size=16)
+    inp = make_inputs(cfg)
+    pf = DevicePrefill(inp, 40)
+    say(f"prefill v3 small {algo} paged={paged}")
+    run(pf, algo)
+    check(pf, weights64(inp), f"v3 small {algo} paged={paged}")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_prefill_v3_two_query_tiles(algo):
+    """130 tokens over 1000 rows: two 128-token tiles, the second with 2."""
+    cfg = V3.with_(name="v3_prefill_130", B=1, ctx=(1000,))
+    inp = make_inputs(cfg)
+    pf = DevicePrefill(inp, 130)
+    say(f"prefill v3 T=130 {algo}")
+    run(pf, algo)
+    check(pf, weights64(inp), f"v3 T=130 {algo}")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_prefill_generic_geometry_and_small_pages(algo):
+    """Shapes off the MFMA kernels: bf16 at another geometry, and a paged cache
+    with 4-row blocks."""
+    cfg = gen.CONFIGS["tiny_fp32"].with_(name="bf16_other", dtype="bf16", H=8, d_c=64, d_R=16, d_h=32, d_v=32,
+                                          B=2, ctx=(70, 33), softmax_scale=0.0)
+    inp = make_inputs(cfg)
+    pf = DevicePrefill(inp, 9)
+    say(f"prefill bf16 other geometry {algo}")
+    run(pf, algo)
+    check(pf, weights64(inp), f"bf16 other {algo}")
+    cfg = V3.with_(name="v3_prefill_pages4", B=2, ctx=(90, 37), paged=True, block_size=4)
+    inp = make_inputs(cfg)
+    pf = DevicePrefill(inp, 12)
+    say(f"prefill v3 4-row pages {algo}")
+    run(pf, algo)
+    check(pf, weights64(inp), f"v3 pages4 {algo}")
+
+
+def test_prefill_full_size_sampled():
+    """The prefill workload (4 sequences of 4096 rows, the newest 512 tokens):
+    sampled tokens of two sequences against the oracle for both algorithms,
+    and the two algorithms against each other on every output."""
+    cfg = gen.CONFIGS["v3_b4_ctx4k_prefill"]
+    inp = make_inputs(cfg)
+    pf = DevicePrefill(inp, 512)
+    W = weights64(inp)
+    outs = {}
+    for algo in ALGOS:
+        say(f"prefill full size {algo}")
+        run(pf, algo)
+        check(pf, W, f"full {algo}", seqs=[0, 3], tokens=[0, 1, 255, 510, 511])
+        outs[algo] = (pf.o.detach().to(torch.float64).cpu().numpy(), pf.lse.cpu().numpy().astype(np.float64))
+    (om_, lm), (oa, la) = outs["materialised"], outs["absorbed"]
+    e = np.abs(om_ - oa).max() / np.abs(oa).max()
+    el = np.abs(lm - la).max() / np.abs(la).max()
+    say(f"materialised vs absorbed: o {e:.2e} lse {el:.2e}")
+    assert e <= 1e-2 and el <= 1e-2
