@@ -35,6 +35,9 @@ namespace {
 #ifndef PREFILL_NW
 #define PREFILL_NW 4           // waves per workgroup
 #endif
+#ifndef PREFILL_NBUF
+#define PREFILL_NBUF 4         // tile buffers in the copy ring
+#endif
 constexpr int KT = 32;         // keys per tile
 constexpr int DH = 128, DR = 64, DV = 128;
 constexpr int DQ = DH + DR;    // query / key width
@@ -82,17 +85,18 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
 }
-__device__ __forceinline__ void wait_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
-// NW waves per workgroup, NQB 32-query MFMA blocks per wave
-template <bool PAGED, int NW, int NQB>
-__global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a, int bs_log2) {
-  constexpr int PT = 64 * NW;
+// NW waves per workgroup, NQB 32-query MFMA blocks per wave, NBUF tile
+// buffers in the copy ring (tiles are fetched NBUF - 1 ahead).
+template <bool PAGED, int NW, int NQB, int NBUF>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(PrefillArgs a, int bs_log2) {
   constexpr int QW = 32 * NQB;   // queries per wave
   constexpr int QT = NW * QW;    // queries per workgroup
-  __shared__ __align__(16) u32x4 lds[2 * BUF_SLOTS];
+  constexpr int KN_CP = KN_SLOTS / 64 / NW, KR_CP = KR_SLOTS / 64 / NW, VT_CP = VT_SLOTS / 64 / NW;
+  constexpr int PW = KN_CP + KR_CP + VT_CP;   // copies per wave per tile
+  static_assert(KN_SLOTS % (64 * NW) == 0 && KR_SLOTS % (64 * NW) == 0 && VT_SLOTS % (64 * NW) == 0, "copy split");
+  __shared__ __align__(16) u32x4 lds[NBUF * BUF_SLOTS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,75 +152,94 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a, in
     for (int j = 0; j < 4; ++j) oacc[qb][j] = f32x16{};
   }
 
-  // Keys of a tile by LDS-DMA: 8 copies of expanded keys (4 rows each) and 4
-  // of rotary keys (8 rows each), split between the two waves; each lane
-  // fetches the chunk that its destination slot holds under the swizzle.
-  // Rows past key_end fetch row key_end - 1 (a real row; every query of the
-  // workgroup masks it out).
+  // One tile by LDS-DMA: expanded keys (4 rows per copy), rotary keys (8 rows
+  // per copy) and transposed values (16 value rows of 32 keys per copy), each
+  // lane fetching the chunk its destination slot holds under the swizzle.
+  // Key rows past key_end fetch row key_end - 1 and value chunks past it the
+  // last chunk holding a valid key (real data in bounds; the keys are masked
+  // and the values zeroed before use).
   const uint32_t lds0 = lds_addr(lds);
-  auto copy_keys = [&](int buf, int u0) {
-    const uint32_t bb = lds0 + buf * BUF_SLOTS * 16;
+  const int last8 = ((key_end - 1) >> 3) << 3;
+  // Paged: the (at most 4, block_size >= 8) blocks of a 32-key tile, read
+  // as scalar loads (through the constant address space, counted by
+  // lgkmcnt) so that the explicit vmcnt waits on the copies stay exact.
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  int tb[4] = {0, 0, 0, 0};
+  int tb0 = 0;
+  auto tile_blocks = [&](int u0) {
+    if constexpr (PAGED) {
+      const const_i32* tab = (const const_i32*)(a.block_table) + static_cast<long long>(b) * a.max_blocks;
+      tb0 = u0 >> bs_log2;
+      const int lastb = (key_end - 1) >> bs_log2;
 #pragma unroll
-    for (int k = 0; k < 8 / NW; ++k) {
-      const int cp = w + NW * k;                      // copy 0..7
+      for (int i = 0; i < 4; ++i) tb[i] = tab[min(tb0 + i, lastb)];
+    }
+  };
+  // storage row of key u (u0 <= u < u0 + 32, u < key_end) of this tile
+  auto srow = [&](int u) -> long long {
+    if constexpr (PAGED) {
+      const int i = (u >> bs_log2) - tb0;
+      const int blk = i == 0 ? tb[0] : i == 1 ? tb[1] : i == 2 ? tb[2] : tb[3];
+      return (static_cast<long long>(blk) << bs_log2) + (u & ((1 << bs_log2) - 1));
+    } else {
+      return static_cast<long long>(b) * a.capacity + u;
+    }
+  };
+  auto copy_tile = [&](int buf, int u0) {
+    const uint32_t bb = lds0 + buf * BUF_SLOTS * 16;
+    tile_blocks(u0);
+#pragma unroll
+    for (int k = 0; k < KN_CP; ++k) {
+      const int cp = w + NW * k;
       const int r = 4 * cp + (lane >> 4);
       const int c = (lane & 15) ^ (r & 15);
       const int u = min(u0 + r, key_end - 1);
-      dma16(Kx + store_row_t<PAGED>(a, b, u, bs_log2) * kstride + head * DH + 8 * c,
+      dma16(Kx + srow(u) * kstride + head * DH + 8 * c,
             __builtin_amdgcn_readfirstlane(bb + cp * 1024));
     }
 #pragma unroll
-    for (int k = 0; k < 4 / NW; ++k) {
-      const int cp = w + NW * k;                      // copy 0..3
+    for (int k = 0; k < KR_CP; ++k) {
+      const int cp = w + NW * k;
       const int r = 8 * cp + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       const int u = min(u0 + r, key_end - 1);
-      dma16(cache + store_row_t<PAGED>(a, b, u, bs_log2) * D + a.d_c + 8 * c,
+      dma16(cache + srow(u) * D + a.d_c + 8 * c,
             __builtin_amdgcn_readfirstlane(bb + KN_SLOTS * 16 + cp * 1024));
     }
-  };
-  // Values through registers (they are reordered on the way to LDS): thread
-  // tid holds 8 keys of value rows tid/4 + (PT/4) j; keys at or past key_end
-  // are zeroed (rows past a sequence may hold anything).
-  constexpr int VJ = DV * 4 / PT;
-  u32x4 st_vt[VJ];
-  const int vg = tid & 3;   // 8-key group of this thread
-  auto load_values = [&](int u0) {
-    const int u = u0 + 8 * vg;
-    long long col = 0;
-    if (u < key_end) {
-      if constexpr (PAGED) col = store_row_t<true>(a, b, u, bs_log2);
-      else col = static_cast<long long>(b) * a.vt_seq + u;
+#pragma unroll
+    for (int k = 0; k < VT_CP; ++k) {
+      const int cp = w + NW * k;
+      const int mrow = 16 * cp + (lane >> 2);
+      const int c = (lane & 3) ^ ((mrow >> 2) & 3);
+      const int u = min(u0 + 8 * c, last8);
+      const long long col = PAGED ? srow(u) : static_cast<long long>(b) * a.vt_seq + u;
+      dma16(Vt + (static_cast<long long>(head) * DV + mrow) * a.vt_ld + col,
+            __builtin_amdgcn_readfirstlane(bb + (KN_SLOTS + KR_SLOTS) * 16 + cp * 1024));
     }
-#pragma unroll
-    for (int j = 0; j < VJ; ++j) {
-      const int mrow = (tid >> 2) + (PT / 4) * j;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (u < key_end) {
-        v = *reinterpret_cast<const u32x4*>(Vt + (static_cast<long long>(head) * DV + mrow) * a.vt_ld + col);
-        if (u + 8 > key_end) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const unsigned lo = (u + 2 * e < key_end) ? 0x0000ffffu : 0u;
-            const unsigned hi = (u + 2 * e + 1 < key_end) ? 0xffff0000u : 0u;
-            v[e] &= lo | hi;
-          }
-        }
+  };
+  // Before computing tile it: this wave's copies of tile it are done
+  // (later tiles' copies may still be in flight), then a barrier publishes
+  // every wave's copies and frees the buffer of tile it - 1 for tile
+  // it + NBUF - 1. The last tile zeroes its value columns past key_end.
+  auto wait_copies = [&](int later) {
+    if (later >= 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * PW) : "memory");
+    else if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PW) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  auto sync_tile = [&](int it, int ntiles) {
+    wait_copies(min(NBUF - 2, ntiles - 1 - it));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (it + NBUF - 1 < ntiles) copy_tile((it + NBUF - 1) % NBUF, (it + NBUF - 1) * KT);
+    if (it == ntiles - 1 && (it + 1) * KT > key_end) {
+      char* Bc = reinterpret_cast<char*>(lds + (it % NBUF) * BUF_SLOTS);
+      const int kv = key_end - it * KT;   // valid keys in this tile
+      for (int e = tid; e < DV * KT; e += 64 * NW) {
+        const int mrow = e / KT, key = e % KT;
+        if (key >= kv)
+          *reinterpret_cast<uint16_t*>(Bc + vt_slot(mrow, key >> 3) * 16 + (key & 7) * 2) = 0;
       }
-      st_vt[j] = v;
-    }
-  };
-  // Key 16kk + 8a + 4hh + c of a value row goes to position 16kk + 8hh + 4a + c
-  // (the S^T register order): keys 8g + 0..3 (g = 2kk + a) to chunk 2kk, keys
-  // 8g + 4..7 to chunk 2kk + 1, both at byte 8a of the chunk.
-  auto store_values = [&](int buf) {
-    char* Bc = reinterpret_cast<char*>(lds + buf * BUF_SLOTS);
-    const int kk = vg >> 1, ah = vg & 1;
-#pragma unroll
-    for (int j = 0; j < VJ; ++j) {
-      const int mrow = (tid >> 2) + (PT / 4) * j;
-      *reinterpret_cast<uint2*>(Bc + vt_slot(mrow, 2 * kk) * 16 + 8 * ah) = uint2{st_vt[j][0], st_vt[j][1]};
-      *reinterpret_cast<uint2*>(Bc + vt_slot(mrow, 2 * kk + 1) * 16 + 8 * ah) = uint2{st_vt[j][2], st_vt[j][3]};
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
   };
 
@@ -253,6 +276,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a, in
   };
   // Softmax weights against the reference m (set from the first tile that
   // has a key; O is still zero then), the normaliser, and O^T += V^T . P^T.
+  // The B operand of k-step kk needs keys 16kk + 8h .. + 7 in lane half h;
+  // the score registers hold keys 16kk + 4h + 0..3 and 16kk + 8 + 4h + 0..3,
+  // so the halves trade one pair of packed words.
   auto weights_and_values = [&](int buf) {
     const u32x4* B = lds + buf * BUF_SLOTS;
     bf16x8 pk[NQB][2];
@@ -270,9 +296,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a, in
       l[qb] += sum + __shfl_xor(sum, 32);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        u32x4 pw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(sacc[qb][8 * kk + 2 * e], sacc[qb][8 * kk + 2 * e + 1]);
+        const uint32_t w0 = pack_bf16x2(sacc[qb][8 * kk + 0], sacc[qb][8 * kk + 1]);
+        const uint32_t w1 = pack_bf16x2(sacc[qb][8 * kk + 2], sacc[qb][8 * kk + 3]);
+        const uint32_t w2 = pack_bf16x2(sacc[qb][8 * kk + 4], sacc[qb][8 * kk + 5]);
+        const uint32_t w3 = pack_bf16x2(sacc[qb][8 * kk + 6], sacc[qb][8 * kk + 7]);
+        const uint32_t s0 = __shfl_xor(h ? w0 : w2, 32);
+        const uint32_t s1 = __shfl_xor(h ? w1 : w3, 32);
+        const u32x4 pw = h ? u32x4{s0, s1, w2, w3} : u32x4{w0, w1, s0, s1};
         pk[qb][kk] = __builtin_bit_cast(bf16x8, pw);
       }
     }
@@ -297,22 +327,17 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a, in
   constexpr float REF_SLACK = 16.f;
   if (key_end > 0) {
     const int ntiles = (key_end + KT - 1) / KT;
-    copy_keys(0, 0);
-    load_values(0);
-    store_values(0);
-    wait_and_barrier();
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < ntiles) copy_tile(t, t * KT);
     int it = 0;
     while (it < ntiles) {
       bool rescale = false;
 #pragma unroll 1
       for (; it < ntiles; ++it) {
-        const bool more = it + 1 < ntiles;
-        if (more) {
-          copy_keys((it + 1) & 1, (it + 1) * KT);
-          load_values((it + 1) * KT);
-        }
+        sync_tile(it, ntiles);
         if (wave_live && it * KT <= wave_qmax) {   // else every key of the tile follows this wave's queries
-          scores(it & 1, it * KT);
+          scores(it % NBUF, it * KT);
           bool over = false;
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) over |= m[qb] != -INFINITY && mx[qb] > m[qb] + REF_SLACK;
@@ -320,10 +345,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a, in
             rescale = true;
             break;
           }
-          weights_and_values(it & 1);
+          weights_and_values(it % NBUF);
         }
-        if (more) store_values((it + 1) & 1);
-        wait_and_barrier();
       }
       if (rescale) {
 #pragma unroll
@@ -335,9 +358,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a, in
           for (int j = 0; j < 4; ++j) oacc[qb][j] *= alpha;
           m[qb] = m_new;
         }
-        weights_and_values(it & 1);
-        if (it + 1 < ntiles) store_values((it + 1) & 1);
-        wait_and_barrier();
+        weights_and_values(it % NBUF);
         ++it;
       }
     }
@@ -467,15 +488,15 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
   if (a.dtype != MLA_BF16 || a.d_h != DH || a.d_R != DR || a.d_v != DV) return hipErrorInvalidValue;
   if (a.block_table && (a.block_size < 8 || (a.block_size & (a.block_size - 1)))) return hipErrorInvalidValue;
   if (a.vt_ld % 8 || a.vt_seq % 8 || (a.d_c + a.d_R) % 8) return hipErrorInvalidValue;
-  constexpr int NQB = PREFILL_NQB, NW = PREFILL_NW;
+  constexpr int NQB = PREFILL_NQB, NW = PREFILL_NW, NBUF = PREFILL_NBUF;
   constexpr int QT = NW * 32 * NQB;
   const long long blocks = static_cast<long long>(a.B) * a.H * ((a.T + QT - 1) / QT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.block_table)
-    prefill_mfma_kernel<true, NW, NQB><<<dim3(static_cast<unsigned>(blocks)), 64 * NW, 0, stream>>>(
+    prefill_mfma_kernel<true, NW, NQB, NBUF><<<dim3(static_cast<unsigned>(blocks)), 64 * NW, 0, stream>>>(
         a, __builtin_ctz(static_cast<unsigned>(a.block_size)));
   else
-    prefill_mfma_kernel<false, NW, NQB><<<dim3(static_cast<unsigned>(blocks)), 64 * NW, 0, stream>>>(a, 0);
+    prefill_mfma_kernel<false, NW, NQB, NBUF><<<dim3(static_cast<unsigned>(blocks)), 64 * NW, 0, stream>>>(a, 0);
   return hipGetLastError();
 }
 
