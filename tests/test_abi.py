@@ -158,3 +158,27 @@ def test_precomposed_argument_errors(L):
     # out_proj_precomposed
     h = lambda ov=A, out=A, wsb=need: L.mla_out_proj_precomposed(ctypes.byref(d), 4, A, ov, out, A, wsb, None)
     assert h(ov=None) == NULL and h(out=None) == NULL and h(out=MIS) == ALIGN and h(wsb=1) == WORKSPACE
+
+
+def test_prefill_argument_errors(L):
+    d = v3()
+    c = mla.MLACache(A, None, 4097, 0, 0, 0)
+    MAT, ABS = mla.PREFILL_MATERIALIZED, mla.PREFILL_ABSORBED
+    need_m = L.mla_prefill_workspace_bytes(ctypes.byref(d), 4, 512, 4096, ctypes.byref(c), MAT)
+    need_a = L.mla_prefill_workspace_bytes(ctypes.byref(d), 4, 512, 4096, ctypes.byref(c), ABS)
+    # materialised: keys and transposed values of every stored row (4 x 4097 rows, 128 heads x 256)
+    assert need_m >= 4 * 4097 * 128 * 256 * 2
+    # absorbed: absorbed queries and fp32 latent outputs of 2048 tokens, plus attention partials
+    assert need_a >= 2048 * 128 * (576 * 2 + 512 * 4)
+    f = lambda B=4, T=512, q=A, sl=A, msl=4096, uk=A, uv=A, algo=MAT, o=A, lse=None, ws=A, wsb=need_m, cache=c: \
+        L.mla_prefill_attn(ctypes.byref(d), B, T, q, ctypes.byref(cache), sl, msl, uk, uv, algo, o, lse, ws, wsb,
+                           None)
+    assert f(q=None) == NULL and f(uk=None) == NULL and f(o=None) == NULL and f(ws=None) == NULL
+    assert f(B=0) == SHAPE and f(T=0) == SHAPE and f(algo=7) == SHAPE and f(msl=5000) == SHAPE
+    assert f(q=MIS) == ALIGN and f(lse=MIS) == ALIGN
+    assert f(wsb=need_m - 1) == WORKSPACE
+    assert f(algo=ABS, wsb=need_a - 1) == WORKSPACE
+    # absorbed form on the MFMA kernel: at most 32768 token entries
+    assert f(B=64, T=1024, algo=ABS, wsb=1 << 40) == UNSUPPORTED
+    assert L.mla_prefill_workspace_bytes(ctypes.byref(d), 64, 1024, 4096, ctypes.byref(c), ABS) == 0
+    assert L.mla_prefill_workspace_bytes(ctypes.byref(d), 4, 0, 4096, ctypes.byref(c), MAT) == 0
