@@ -749,28 +749,51 @@ void attn_mfma_kernel(Params p) {
   __syncthreads();
   // The accumulators are read next; cover the last MFMAs' latency.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // Epilogue through LDS (the tile stages are free now), 64 heads per
+  // round: each wave writes its accumulator blocks of those heads into
+  // head rows of 512 floats, then the workgroup stores the rows as one
+  // contiguous run, 16 bytes per lane, so every store instruction writes
+  // 1 KiB of consecutive output (16-byte pieces of 32 head rows per
+  // instruction straight from the accumulators left HBM lines half written).
   // D[i][head] of block (c, hb) holds column colbase(4w + c) + 32*((i&15)>>2)
   // + 4*(i>>4) + (i&3); register 4g + m of this lane is i = 8g + 4h + m.
+  constexpr int OROW = 2 * 1024 + 16;   // staged row stride: rows 16 B apart on the banks
+  static_assert(64 * OROW <= LM_OFF, "staged rows must not reach the per-head (m, l)");
+  float* obase = single ? p.o_lat + static_cast<long long>(b) * p.H * DC
+                        : p.part_o + static_cast<long long>(gi) * p.H * DC;
 #pragma unroll
-  for (int hb = 0; hb < NW; ++hb) {
-    const int head = 32 * hb + l32;
-    const float inv = single ? 1.f / lm[2 * head + 1] : 1.f;
-    float* o = single ? p.o_lat + (static_cast<long long>(b) * p.H + head) * DC
-                      : p.part_o + (static_cast<long long>(gi) * p.H + head) * DC;
+  for (int R = 0; R < (NW + 1) / 2; ++R) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float x[16];
+    for (int hh = 0; hh < 2; ++hh) {
+      const int hb = 2 * R + hh;
+      if (hb < NW) {
+        const int head = 32 * hb + l32;
+        const float inv = single ? 1.f / lm[2 * head + 1] : 1.f;
+        char* rowp = smem + (32 * hh + l32) * OROW;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[4 * c + hb][r]));
+        for (int c = 0; c < 4; ++c) {
+          float x[16];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = colbase(4 * w + c) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
-        // plain stores: these 16-byte pieces of 32 head rows complete their
-        // lines across the wave's stores, in L2
-        *reinterpret_cast<f32x4*>(o + col) =
-            f32x4{x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv};
+          for (int r = 0; r < 16; ++r)
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[4 * c + hb][r]));
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = colbase(4 * w + c) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
+            *reinterpret_cast<f32x4*>(rowp + 4 * col) =
+                f32x4{x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv};
+          }
+        }
       }
     }
+    __syncthreads();
+    const int nrows = min(64, p.H - 64 * R);
+    float* dst = obase + 64LL * R * DC;
+    for (int idx = tid; idx < nrows * (DC / 4); idx += NTHREADS) {
+      const int row = idx >> 7, piece = idx & 127;
+      *reinterpret_cast<f32x4*>(dst + row * DC + 4 * piece) =
+          *reinterpret_cast<const f32x4*>(smem + row * OROW + 16 * piece);
+    }
+    __syncthreads();
   }
 }
 
