@@ -187,7 +187,7 @@ class MLAInputs:
             return self.cache[b, :n]
         bs = self.cfg.block_size
         nb = (n + bs - 1) // bs
-        pages = self.cache[self.block_table[b, :nb]].reshape(nb * bs, -1)
+        pages = self.cache[self.block_table[b, :nb]].reshape(nb * bs, self.cache.shape[-1])
         return pages[:n]
 
 

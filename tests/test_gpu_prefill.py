@@ -68,22 +68,26 @@ def run(pf, algo_name):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("algo", list(ALGOS))
-def test_prefill_tiny_fp32(algo):
-    cfg = gen.CONFIGS["tiny_fp32"].with_(ctx=(64,))
+def test_prefill_tiny_fp32(algo, paged):
+    """fp32 storage (plain kernels), contiguous and 4-row pages, with a
+    sequence that holds no row at all."""
+    cfg = gen.CONFIGS["tiny_fp32"].with_(B=3, ctx=(64, 0, 3), paged=paged, block_size=4)
     inp = make_inputs(cfg)
     pf = DevicePrefill(inp, 5)
-    say(f"prefill tiny_fp32 {algo} T=5")
+    say(f"prefill tiny_fp32 {algo} paged={paged} T=5")
     run(pf, algo)
-    check(pf, weights64(inp), f"tiny {algo}")
+    check(pf, weights64(inp), f"tiny {algo} paged={paged}")
 
 
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("algo", list(ALGOS))
 def test_prefill_v3_small_ragged(algo, paged):
-    """Three sequences of 45, 300 and 7 rows, 40 tokens each: a partial query
-    tile, masked diagonal tiles, and a sequence with fewer rows than tokens."""
-    cfg = V3.with_(name="v3_prefill_small", B=3, ctx=(45, 300, 7), paged=paged, block_size=16)
+    """Sequences of 45, 300, 7 and 0 rows, 40 tokens each: a partial query
+    tile, masked diagonal tiles, a sequence with fewer rows than tokens and
+    one with none (its workgroups have nothing to attend)."""
+    cfg = V3.with_(name="v3_prefill_small", B=4, ctx=(45, 300, 7, 0), paged=paged, block_size=16)
     inp = make_inputs(cfg)
     pf = DevicePrefill(inp, 40)
     say(f"prefill v3 small {algo} paged={paged}")
