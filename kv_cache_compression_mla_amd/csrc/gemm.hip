@@ -469,28 +469,52 @@ __global__ void reduce_store_kernel(const float* __restrict__ P, int splits, int
 
 // Rotary projection [M][G*d_R] -> rotated, stored at out[m*ldo + g*sOg + j].
 template <typename TO>
-__global__ void reduce_rope_kernel(const float* __restrict__ P, int splits, int M, int G, int d_R,
-                                   const int32_t* __restrict__ pos, float theta,
-                                   TO* __restrict__ out, long long ldo, long long sOg) {
-  const long long idx = blockIdx.x * 256LL + threadIdx.x;   // pair index
+__global__ __launch_bounds__(256) void reduce_rope_kernel(const float* __restrict__ P, int splits, int M, int G,
+                                                          int d_R, const int32_t* __restrict__ pos, float theta,
+                                                          TO* __restrict__ out, long long ldo, long long sOg) {
+  // Workgroup (chunk x, row m): pairs 256x .. 256x + 255 of row m, one per
+  // thread, all split loads of a thread in flight together. The angle of
+  // pair j depends on (m, j) only: the workgroup evaluates each angle it
+  // needs once and every head in the chunk reuses it.
+  __shared__ float cs[2 * 512];
   const int half = d_R / 2;
-  const long long total_pairs = static_cast<long long>(M) * G * half;
-  if (idx >= total_pairs) return;
-  const int j = static_cast<int>(idx % half);
-  const int g = static_cast<int>((idx / half) % G);
-  const int m = static_cast<int>(idx / (static_cast<long long>(half) * G));
+  const int row_pairs = G * half;
   const long long total = static_cast<long long>(M) * G * d_R;
-  const long long e0 = (static_cast<long long>(m) * G + g) * d_R + 2 * j;
-  float x0 = 0.f, x1 = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    x0 += P[s * total + e0];
-    x1 += P[s * total + e0 + 1];
+  const int p0 = blockIdx.x * 256;
+  const int nj = min(half, 256);
+  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+    for (int t = threadIdx.x; t < nj; t += 256) {
+      const int j = (half <= 256) ? t : (p0 + t) % half;
+      rope_cs(pos[m], j, d_R, theta, &cs[2 * t], &cs[2 * t + 1]);
+    }
+    __syncthreads();
+    const int pi = p0 + threadIdx.x;
+    if (pi < row_pairs) {
+      const int g = pi / half, j = pi % half;
+      const int jt = (half <= 256) ? j : pi - p0;
+      const long long e0 = static_cast<long long>(m) * G * d_R + 2LL * pi;
+      float x0 = 0.f, x1 = 0.f;
+      int s = 0;
+      for (; s + 4 <= splits; s += 4) {
+        const float2 v0 = *reinterpret_cast<const float2*>(P + s * total + e0);
+        const float2 v1 = *reinterpret_cast<const float2*>(P + (s + 1) * total + e0);
+        const float2 v2 = *reinterpret_cast<const float2*>(P + (s + 2) * total + e0);
+        const float2 v3 = *reinterpret_cast<const float2*>(P + (s + 3) * total + e0);
+        x0 += v0.x + v1.x + v2.x + v3.x;
+        x1 += v0.y + v1.y + v2.y + v3.y;
+      }
+      for (; s < splits; ++s) {
+        const float2 v = *reinterpret_cast<const float2*>(P + s * total + e0);
+        x0 += v.x;
+        x1 += v.y;
+      }
+      const float c = cs[2 * jt], sn = cs[2 * jt + 1];
+      TO* o = out + static_cast<long long>(m) * ldo + g * sOg + 2 * j;
+      Elem<TO>::st(o, x0 * c - x1 * sn);
+      Elem<TO>::st(o + 1, x0 * sn + x1 * c);
+    }
+    __syncthreads();   // the angles of the next row overwrite cs
   }
-  float c, sn;
-  rope_cs(pos[m], j, d_R, theta, &c, &sn);
-  TO* o = out + m * ldo + g * sOg + 2 * j;
-  Elem<TO>::st(o, x0 * c - x1 * sn);
-  Elem<TO>::st(o + 1, x0 * sn + x1 * c);
 }
 
 // One workgroup per sequence, one thread per column of the row (up to 1024):
@@ -719,8 +743,9 @@ hipError_t launch_reduce_store(const float* P, int splits, int G, int M, int N, 
 hipError_t launch_reduce_rope(const float* P, int splits, int M, int G, int d_R, const int32_t* pos,
                               float theta, void* out, long long ldo, long long sOg, int out_dtype,
                               hipStream_t stream) {
-  const long long pairs = static_cast<long long>(M) * G * (d_R / 2);
-  const dim3 grid(static_cast<unsigned>((pairs + 255) / 256));
+  if (d_R > 1024 || d_R % 2) return hipErrorInvalidValue;
+  const long long row_pairs = static_cast<long long>(G) * (d_R / 2);
+  const dim3 grid(static_cast<unsigned>((row_pairs + 255) / 256), static_cast<unsigned>(M < 65535 ? M : 65535));
   if (out_dtype == MLA_BF16)
     reduce_rope_kernel<uint16_t><<<grid, 256, 0, stream>>>(P, splits, M, G, d_R, pos, theta, static_cast<uint16_t*>(out), ldo, sOg);
   else

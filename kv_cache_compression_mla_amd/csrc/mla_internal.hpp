@@ -42,15 +42,21 @@ template <> struct Elem<uint16_t> {
 };
 
 // Rotary angle cos/sin for pair j of a d_R-wide vector at integer position
-// pos: angle = pos * theta^(-2j/d_R). Evaluated in double so that long
-// contexts (angles up to ~3e4 rad) keep full float32 accuracy.
+// pos: angle = pos * theta^(-2j/d_R). The angle (up to ~3e4 rad at long
+// contexts) is formed and reduced to [-pi, pi] in double: the frequency as
+// exp2(-(2j/d_R) log2 theta), then Cody-Waite reduction by a two-part 2*pi
+// (a rounded multiple k of 2*pi removed with two fused multiply-adds), so the
+// reduced angle is accurate to ~1e-12 rad; float32 sincos of it is then
+// accurate to about one float32 ulp, far below the bf16 rounding of the
+// rotated values.
 __device__ __forceinline__ void rope_cs(int pos, int j, int d_R, float theta, float* c, float* s) {
-  double inv = pow(static_cast<double>(theta), -2.0 * j / d_R);
-  double a = static_cast<double>(pos) * inv;
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  *c = static_cast<float>(cd);
-  *s = static_cast<float>(sd);
+  const double inv = exp2(-(2.0 * j / d_R) * log2(static_cast<double>(theta)));
+  const double a = static_cast<double>(pos) * inv;
+  constexpr double kTwoPiHi = 6.283185307179586;          // double nearest 2*pi
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;     // 2*pi - kTwoPiHi
+  const double k = rint(a * (1.0 / kTwoPiHi));
+  const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, a));
+  sincosf(static_cast<float>(r), s, c);
 }
 
 // ---------------------------------------------------------------------------
