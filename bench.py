@@ -9,8 +9,10 @@ synthetic tensors of the DeepSeek-V3 geometry, resident in HBM before timing.
 Headline: decode-attention TFLOP/s (algorithmic FLOPs 2*H*(D + d_c) per
 attended row) and latent-cache GB/s (1152 B per attended row) of the
 mla_decode_attn call, both from HIP events recorded on the stream the library
-launches on; ms_per_step is the whole step and calls_ms the mean time of each
-of the four calls (events between them). The roofline object prices the
+launches on; ms_per_step is the whole step (wall clock over the K timed
+steps, whose only events are the two around the attention call) and calls_ms
+the mean time of each of the four calls from a separate untimed pass with
+events between them. The roofline object prices the
 attention call against MI355X's published HBM bandwidth (8 TB/s); the CPU
 baseline times the float64 oracle on a bounded sample of the same workload.
 
@@ -198,16 +200,32 @@ def main():
     log(f"B={cfg.B} rows={rows} splits={splits} kernel={mla.decode_kernel(st.dims)}")
 
     stream = torch.cuda.current_stream()
-    # events between the four calls, all on the stream the library launches on
-    calls = ("compress_append", "absorb_q", "decode_attn", "out_proj")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    # timed region: K whole steps; the only events in it are the two around
+    # the attention call (each event is a marker packet that costs the
+    # stream a few microseconds, so per-call events would inflate the step)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
 
     t_start = time.perf_counter()
     for k in range(args.steps):
-        e = ev[k]
+        st.compress_append()
+        st.absorb_q()
+        ev[k][0].record(stream)
+        st.decode_attn()
+        ev[k][1].record(stream)
+        st.out_proj()
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = t_total * 1e3 / args.steps
+
+    # per-call breakdown, after the timed region: events between all four calls
+    calls = ("compress_append", "absorb_q", "decode_attn", "out_proj")
+    nb = min(args.steps, 10)
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(nb)]
+    for e in evc:
         e[0].record(stream)
         st.compress_append()
         e[1].record(stream)
@@ -218,11 +236,8 @@ def main():
         st.out_proj()
         e[4].record(stream)
     torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
-    calls_ms = {c: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])), 5)
+    calls_ms = {c: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evc])), 5)
                 for i, c in enumerate(calls)}
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    ms_per_step = t_total * 1e3 / args.steps
 
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     cache_gbps = cache_bytes / (attn_ms * 1e-3) / 1e9
