@@ -29,6 +29,9 @@
 namespace mla {
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 #ifndef PREFILL_NQB
 #define PREFILL_NQB 1          // 32-query MFMA blocks per wave
 #endif
@@ -247,31 +250,55 @@ void prefill_mfma_kernel(PrefillArgs a, int bs_log2) {
   // mx: each query's largest score in the tile.
   f32x16 sacc[NQB];
   float mx[NQB];
+  // The 12 k-steps run as two interleaved accumulation chains (even and odd
+  // steps, summed at the end) so that consecutive MFMAs do not wait on each
+  // other's results, with the key operands read PF steps ahead.
+  constexpr int PF = 4;
   auto scores = [&](int buf, int u0) {
     const u32x4* B = lds + buf * BUF_SLOTS;
+    auto operand = [&](int s) -> u32x4 {
+      return s < DH / 16 ? B[kn_slot(l32, 2 * s + h)] : B[kr_slot(l32, 2 * (s - DH / 16) + h)];
+    };
+    f32x16 sodd[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) sacc[qb] = f32x16{};
+    for (int qb = 0; qb < NQB; ++qb) {
+      sacc[qb] = f32x16{};
+      sodd[qb] = f32x16{};
+    }
+    u32x4 ops[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) ops[i] = operand(i);
 #pragma unroll
     for (int s = 0; s < SK; ++s) {
-      const u32x4 av = s < DH / 16 ? B[kn_slot(l32, 2 * s + h)] : B[kr_slot(l32, 2 * (s - DH / 16) + h)];
+      const u32x4 av = ops[s % PF];
+      if (s + PF < SK) ops[s % PF] = operand(s + PF);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), qr[qb][s], sacc[qb],
-                                                           0, 0, 0);
+      for (int qb = 0; qb < NQB; ++qb) {
+        if (s & 1)
+          sodd[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), qr[qb][s], sodd[qb],
+                                                             0, 0, 0);
+        else
+          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), qr[qb][s], sacc[qb],
+                                                             0, 0, 0);
+      }
     }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) sacc[qb] += sodd[qb];
     const bool need_mask = u0 + KT - 1 > wave_qmin;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      // lane (h, l32) holds query l32's scores of keys 8(r/4) + 4h + r%4
-      float x = -INFINITY;
+      // lane (h, l32) holds query l32's raw scores of keys 8(r/4) + 4h + r%4;
+      // the maximum is taken on raw scores (the scale is positive) and
+      // scaled once
+      if (need_mask) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = sacc[qb][r] * sl2;
-        if (need_mask && u0 + 8 * (r >> 2) + 4 * h + (r & 3) > qpos[qb]) sv = -INFINITY;
-        sacc[qb][r] = sv;
-        x = fmaxf(x, sv);
+        for (int r = 0; r < 16; ++r)
+          if (u0 + 8 * (r >> 2) + 4 * h + (r & 3) > qpos[qb]) sacc[qb][r] = -INFINITY;
       }
-      mx[qb] = fmaxf(x, __shfl_xor(x, 32));
+      float x = sacc[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) x = fmaxf(x, sacc[qb][r]);
+      mx[qb] = fmaxf(x, __shfl_xor(x, 32)) * sl2;
     }
   };
   // Softmax weights against the reference m (set from the first tile that
@@ -286,20 +313,25 @@ void prefill_mfma_kernel(PrefillArgs a, int bs_log2) {
     for (int qb = 0; qb < NQB; ++qb) {
       if (m[qb] == -INFINITY) m[qb] = mx[qb];
       const float mref = m[qb] == -INFINITY ? 0.f : m[qb];   // no key yet: every p is 0
+      // weight 2^(s * sl2 - mref): one fma and the hardware exp2 (masked
+      // scores are -inf and give 0; weights are at most 2^REF_SLACK)
       float sum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = exp2f(sacc[qb][r] - mref);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], sl2, -mref));
         sacc[qb][r] = pv;
         sum += pv;
       }
       l[qb] += sum + __shfl_xor(sum, 32);
+      auto pk2 = [](float a, float b) -> uint32_t {   // nearest-even bf16 pair (v_cvt_pk_bf16_f32)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+      };
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint32_t w0 = pack_bf16x2(sacc[qb][8 * kk + 0], sacc[qb][8 * kk + 1]);
-        const uint32_t w1 = pack_bf16x2(sacc[qb][8 * kk + 2], sacc[qb][8 * kk + 3]);
-        const uint32_t w2 = pack_bf16x2(sacc[qb][8 * kk + 4], sacc[qb][8 * kk + 5]);
-        const uint32_t w3 = pack_bf16x2(sacc[qb][8 * kk + 6], sacc[qb][8 * kk + 7]);
+        const uint32_t w0 = pk2(sacc[qb][8 * kk + 0], sacc[qb][8 * kk + 1]);
+        const uint32_t w1 = pk2(sacc[qb][8 * kk + 2], sacc[qb][8 * kk + 3]);
+        const uint32_t w2 = pk2(sacc[qb][8 * kk + 4], sacc[qb][8 * kk + 5]);
+        const uint32_t w3 = pk2(sacc[qb][8 * kk + 6], sacc[qb][8 * kk + 7]);
         const uint32_t s0 = __shfl_xor(h ? w0 : w2, 32);
         const uint32_t s1 = __shfl_xor(h ? w1 : w3, 32);
         const u32x4 pw = h ? u32x4{s0, s1, w2, w3} : u32x4{w0, w1, s0, s1};

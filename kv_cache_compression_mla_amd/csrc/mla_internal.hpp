@@ -26,9 +26,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
 }
-// Two floats -> packed bf16 pair (lo = a, hi = b), nearest-even.
+// Two floats -> packed bf16 pair (lo = a, hi = b), nearest-even: one
+// v_cvt_pk_bf16_f32 on gfx950 (same rounding as f32_to_bf16 for every
+// non-NaN value; NaN stays NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{a, b}), v2bf));
 }
 
 template <typename T> struct Elem;
