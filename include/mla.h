@@ -292,7 +292,7 @@ mla_status mla_out_proj_precomposed(const mla_dims* dims, int32_t B, const float
  *          (d_h + d_v) * H elements per row.
  * Errors: MLA_ERR_SHAPE for B, T <= 0, an unknown algo or max_seq_len above
  * the cache; MLA_ERR_UNSUPPORTED if B * T exceeds 32768 (absorbed, V3
- * geometry) or the cache has more than 2^31 - 1 rows (materialised).
+ * geometry) or the cache stores more than 8,388,480 rows (materialised).
  */
 typedef enum { MLA_PREFILL_MATERIALIZED = 0, MLA_PREFILL_ABSORBED = 1 } mla_prefill_algo;
 

@@ -617,6 +617,8 @@ bool mfma_ok(const GemmArgs& a) {
   return true;
 }
 
+// The streaming kernel is for skinny products (every workgroup re-streams its
+// activation rows for each column tile); taller products take the tiled kernel.
 bool stream_ok(const GemmArgs& a) { return mfma_ok(a) && !a.w_kn && a.K % SKT == 0 && a.M <= 128; }
 
 int device_cus() {
@@ -662,6 +664,8 @@ bool gemm_concat_ok(const GemmArgs& a) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.W2 && !gemm_concat_ok(a)) return hipErrorInvalidValue;
+  // m blocks (of up to 128 rows) times k splits share the z grid dimension
+  if (static_cast<long long>(a.splits) * ((a.M + 127) / 128) > 65535) return hipErrorInvalidValue;
   const int splits = a.splits;
   const int ksteps = (a.K + GBK - 1) / GBK;
   const int kper = ((ksteps + splits - 1) / splits) * GBK;
@@ -676,7 +680,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     }
     const int MT = a.M <= 32 ? 1 : a.M <= 64 ? 2 : 4;
     const int nt = stream_nt(a.N);
-    const dim3 grid((a.N + nt - 1) / nt, a.G, splits);
+    const int mblocks = (a.M + 32 * MT - 1) / (32 * MT);
+    const dim3 grid((a.N + nt - 1) / nt, a.G, splits * mblocks);
 #define MLA_STREAM(NTV, MTV)                                                                     \
   if (a.a_f32) gemm_stream_kernel<NTV, MTV, true><<<grid, GTH, 0, stream>>>(p);                  \
   else gemm_stream_kernel<NTV, MTV, false><<<grid, GTH, 0, stream>>>(p);

@@ -532,7 +532,7 @@ PrefillPlan prefill_plan(const mla_dims* d, int B, int T, int max_seq_len, const
   return pl;
 }
 
-constexpr long long kMaxPrefillRows = 0x7fffffffLL;
+constexpr long long kMaxPrefillRows = 65535LL * 128;   // rows one expansion product takes (128 per z block)
 
 mla_status check_prefill_sizes(const mla_dims* d, int B, int T, int max_seq_len, const mla_cache* c, int algo) {
   if (B <= 0 || T <= 0) return fail(MLA_ERR_SHAPE, "prefill: B and T must be positive");
