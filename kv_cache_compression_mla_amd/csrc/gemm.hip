@@ -427,6 +427,130 @@ __global__ __launch_bounds__(GTH) void gemm_stream_kernel(GemmP p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tall products (many rows of activations, e.g. expanding every cached
+// latent row into per-head keys or values): bf16 A [M][K] (lda) times bf16
+// W [N][K] (ldw), stored directly as bf16 out[g*sOg + m*ldo + n]; K a
+// multiple of 64, one k range. A workgroup owns a 128 (n) x 128 (m) tile;
+// its four waves own 64 x 64 each (2 x 2 MFMA 32x32x16 blocks, four operand
+// reads per four MFMAs). Stages of 64 k (16 KiB of weights, 16 KiB of
+// activations) go HBM -> LDS by LDS-DMA, double buffered, with the same
+// swizzle as the streaming kernel; 64 KiB of LDS lets two workgroups share
+// a CU, so one's prologue and stores overlap the other's MFMAs. The
+// epilogue stages the tile in LDS as rows of 128 outputs and stores each row
+// as one contiguous 256-byte run.
+// ---------------------------------------------------------------------------
+constexpr int TT_N = 128, TT_M = 128;
+constexpr int TT_WB = TT_N * 128, TT_AB = TT_M * 128;     // bytes per stage
+constexpr int TT_STAGE = TT_WB + TT_AB;                   // 48 KiB
+constexpr int TT_NS = 2;
+constexpr int TT_PW = TT_STAGE / 1024 / 4;                 // copies per wave per stage: 12
+constexpr int TT_OROW = TT_N * 2 + 16;                    // staged output row stride (bytes)
+static_assert(TT_M * TT_OROW <= TT_NS * TT_STAGE, "output tile fits in the ring");
+
+__global__ __launch_bounds__(256) void gemm_tall_kernel(const uint16_t* __restrict__ A, long long lda,
+                                                        long long sAg, const uint16_t* __restrict__ W,
+                                                        long long ldw, long long sWg, uint16_t* __restrict__ out,
+                                                        long long ldo, long long sOg, int M, int N, int K) {
+  __shared__ __align__(1024) char smem[TT_NS * TT_STAGE];
+  const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)smem));
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5, l32 = lane & 31;
+  const int wn = w & 1, wm = w >> 1;
+  const int n0 = blockIdx.x * TT_N, m0 = blockIdx.y * TT_M, g = blockIdx.z;
+  const uint16_t* Wg = W + g * sWg;
+  const uint16_t* Ag = A + g * sAg;
+  const int nsteps = K / 64;
+
+  auto issue_stage = [&](int t) {
+    const int kb = t * 64;
+    const uint32_t st = sbase + (t % TT_NS) * TT_STAGE;
+#pragma unroll
+    for (int j = 0; j < TT_PW; ++j) {
+      const int i = w * TT_PW + j;                   // copy 0..47
+      const int r8 = lane >> 3, c = (lane & 7);
+      if (i < TT_N / 8) {                            // weight rows 8i..8i+7
+        const int r = 8 * i + r8;
+        const int n = min(n0 + r, N - 1);
+        dma_copy(Wg + static_cast<long long>(n) * ldw + kb + 8 * (c ^ ((r >> 1) & 7)), st + 1024 * i);
+      } else {                                       // activation rows
+        const int a = i - TT_N / 8, r = 8 * a + r8;
+        const int m = min(m0 + r, M - 1);
+        dma_copy(Ag + static_cast<long long>(m) * lda + kb + 8 * (c ^ ((r >> 1) & 7)), st + TT_WB + 1024 * a);
+      }
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+#pragma unroll
+  for (int t = 0; t < TT_NS - 1; ++t)
+    if (t < nsteps) issue_stage(t);
+  for (int t = 0; t < nsteps; ++t) {
+    wait_later<TT_PW, TT_NS - 2>(min(nsteps - 1 - t, TT_NS - 2));
+    asm volatile("s_barrier" ::: "memory");
+    if (t + TT_NS - 1 < nsteps) issue_stage(t + TT_NS - 1);
+    const char* st = smem + (t % TT_NS) * TT_STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {                    // k16 steps of the stage
+      const int cw = 2 * j + h;
+      u32x4 wv[2], av[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int rw = 64 * wn + 32 * nb + l32;
+        wv[nb] = *reinterpret_cast<const u32x4*>(st + 16 * (rw * 8 + (cw ^ ((rw >> 1) & 7))));
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int ra = 64 * wm + 32 * mb + l32;
+        av[mb] = *reinterpret_cast<const u32x4*>(st + TT_WB + 16 * (ra * 8 + (cw ^ ((ra >> 1) & 7))));
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv[nb]),
+                                                                __builtin_bit_cast(bf16x8, av[mb]), acc[nb][mb],
+                                                                0, 0, 0);
+    }
+  }
+  // D[n][m] of block (nb, mb): lane holds m = 32mb + l32, n = 32nb + 8(r/4) + 4h + r%4
+  // (within the wave's 128 x 64). Stage as rows m of 256 outputs, then store rows.
+  __syncthreads();
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int ml = 64 * wm + 32 * mb + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = 64 * wn + 32 * nb + 8 * q + 4 * h;
+        *reinterpret_cast<uint2*>(smem + ml * TT_OROW + 2 * nl) =
+            make_uint2(pack_bf16x2(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1]),
+                       pack_bf16x2(acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]));
+      }
+    }
+  __syncthreads();
+  uint16_t* og = out + g * sOg;
+  for (int idx = tid; idx < TT_M * (TT_N / 8); idx += 256) {
+    const int row = idx / (TT_N / 8), piece = idx % (TT_N / 8);
+    const int m = m0 + row, n = n0 + 8 * piece;
+    if (m >= M || n >= N) continue;
+    const char* src = smem + row * TT_OROW + 16 * piece;
+    uint16_t* dst = og + static_cast<long long>(m) * ldo + n;
+    if (n + 8 <= N && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = reinterpret_cast<const uint16_t*>(src)[e];
+    }
+  }
+}
+
 // One thread per output element (fp32 storage, or shapes the MFMA kernel
 // does not take). Same partial layout as the MFMA kernel.
 template <typename TA, typename TW>
@@ -731,6 +855,22 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
         static_cast<const float*>(a.A), a.lda, a.sAg, static_cast<const float*>(a.W), a.ldw, a.sWg,
         a.w_kn, a.M, a.N, a.K, a.G, kper, a.P);
   }
+  return hipGetLastError();
+}
+
+bool gemm_tall_ok(const GemmArgs& a) {
+  return a.dtype == MLA_BF16 && !a.a_f32 && !a.w_kn && !a.W2 && a.out && a.out_dtype == MLA_BF16 && a.K % 64 == 0 &&
+         a.M > 128 && a.lda % 8 == 0 && a.ldw % 8 == 0 && a.sAg % 8 == 0 && a.sWg % 8 == 0 &&
+         ((reinterpret_cast<uintptr_t>(a.A) | reinterpret_cast<uintptr_t>(a.W)) & 15) == 0 &&
+         (a.M + TT_M - 1) / TT_M <= 65535 && a.G <= 65535;
+}
+
+hipError_t launch_gemm_tall(const GemmArgs& a, hipStream_t stream) {
+  if (!gemm_tall_ok(a)) return hipErrorInvalidValue;
+  const dim3 grid((a.N + TT_N - 1) / TT_N, (a.M + TT_M - 1) / TT_M, a.G);
+  gemm_tall_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(a.A), a.lda, a.sAg,
+                                             static_cast<const uint16_t*>(a.W), a.ldw, a.sWg,
+                                             static_cast<uint16_t*>(a.out), a.ldo, a.sOg, a.M, a.N, a.K);
   return hipGetLastError();
 }
 

@@ -571,19 +571,26 @@ mla_status prefill_materialized(const mla_dims* d, int B, int T, const void* q, 
   const long long rows = cache_store_rows(c, B);
   const bool paged = c->block_table != nullptr;
   const long long vt_ld = vt_row_len(c, B), vt_seq = vt_seq_stride(c);
+  // Expansion products: the tall kernel when it takes the shape, else the
+  // general GEMM with its own store.
+  auto expand = [&](const void* Am, long long lda, long long sAg, const void* Wm, long long ldw, long long sWg,
+                    const GemmShape& s, void* out, long long ldo, long long sOg) -> mla_status {
+    mla::GemmArgs g{Am, lda, sAg, f32, Wm, ldw, sWg, false, s.M, s.N, s.K, s.G, 1, P, dt};
+    g.out = out;
+    g.ldo = ldo;
+    g.sOg = sOg;
+    g.out_dtype = dt;
+    if (mla::gemm_tall_ok(g)) return hip_status(mla::launch_gemm_tall(g, st), "gemm launch");
+    return gemm_store(Am, lda, sAg, f32, Wm, ldw, sWg, false, s, dt, P, out, ldo, sOg, st);
+  };
   // K[row][i*d_h + k] = (W_UK(i) c_row)[k] for every stored row
-  {
-    const GemmShape s{static_cast<int>(rows), H * d->d_h, d->d_c, 1};
-    MLA_TRY(gemm_store(c->data, D, 0, f32, W_UK, d->d_c, 0, false, s, dt, P, Kx, static_cast<long long>(H) * d->d_h,
-                       0, st));
-  }
+  MLA_TRY(expand(c->data, D, 0, W_UK, d->d_c, 0, GemmShape{static_cast<int>(rows), H * d->d_h, d->d_c, 1}, Kx,
+                 static_cast<long long>(H) * d->d_h, 0));
   // Vt[i*d_v + j][col] = (W_UV(i) c_row)[j]: W_UV times the rows, per sequence
   // (contiguous) or over the whole pool (paged)
-  {
-    const GemmShape s{H * d->d_v, paged ? static_cast<int>(rows) : c->capacity, d->d_c, paged ? 1 : B};
-    MLA_TRY(gemm_store(W_UV, d->d_c, 0, f32, c->data, D, paged ? 0 : static_cast<long long>(c->capacity) * D, false,
-                       s, dt, P, Vt, vt_ld, paged ? 0 : vt_seq, st));
-  }
+  MLA_TRY(expand(W_UV, d->d_c, 0, c->data, D, paged ? 0 : static_cast<long long>(c->capacity) * D,
+                 GemmShape{H * d->d_v, paged ? static_cast<int>(rows) : c->capacity, d->d_c, paged ? 1 : B}, Vt,
+                 vt_ld, paged ? 0 : vt_seq));
   mla::PrefillArgs a{};
   a.q = q;
   a.K = Kx;

@@ -94,6 +94,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 bool gemm_direct(const GemmArgs& a);
 // True when launch_gemm can take a's second weight (W2, n_split).
 bool gemm_concat_ok(const GemmArgs& a);
+// Tall bf16 products stored directly (out set; the P, splits and W2 fields
+// are not used): more than 128 rows of A, NT weights, K a multiple of 64.
+bool gemm_tall_ok(const GemmArgs& a);
+hipError_t launch_gemm_tall(const GemmArgs& a, hipStream_t stream);
 // Number of k splits launch_gemm would pick for a shape (used to size workspaces).
 int gemm_splits(int M, int N, int K, int G, int dtype);
 
