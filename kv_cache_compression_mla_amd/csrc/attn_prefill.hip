@@ -12,18 +12,20 @@
 //   s(u) = scale * (q_C . K_nope(u) + q_R . k_R(u))   u = 0..p
 //   o    = sum_u softmax(s)(u) V(u),  lse = ln sum_u exp s(u).
 //
-// MFMA kernel (bf16, d_h = d_v = 128, d_R = 64): one workgroup of two waves
-// per (sequence, head, 128-query tile); each wave owns 64 queries (two
-// 32-query MFMA blocks). 32-key tiles of the expanded keys, the rotary keys
-// and the transposed values go HBM -> registers -> LDS (double buffered, one
-// barrier per tile) and are shared by both waves. Per tile and query block:
-//   S^T = K . Q^T   (32 keys x 32 queries, 12 MFMA 32x32x16 over 192 features)
+// MFMA kernel (bf16, d_h = d_v = 128, d_R = 64): one workgroup of four waves
+// per (sequence, head, 128-query tile), 32 queries per wave. 32-key tiles of
+// the expanded keys, the rotary keys and the transposed values go HBM -> LDS
+// by LDS-DMA through a ring of four buffers (fetched three tiles ahead, one
+// barrier per tile; 80 KiB, two workgroups per CU) and are shared by the four
+// waves. Per tile and wave:
+//   S^T = K . Q^T    (32 keys x 32 queries, 12 MFMA 32x32x16 over 192 features)
 //   O^T += V^T . P^T (128 d_v x 32 queries, 8 MFMA over 32 keys)
-// with an online softmax per query held in the lane that owns the query's
-// column, so the rescale of O touches only that lane's registers. Within
-// each 16-key half of a tile the keys are ordered as the S^T accumulator
-// holds them, so the probabilities feed the value MFMA straight from the
-// score registers; the staging writes the value columns in that order.
+// with the softmax of a query held in the lane that owns its column. The
+// weights use a fixed per-query reference (rescaled only when a tile's
+// maximum exceeds it by 2^16), so O is written only by MFMA in the tile
+// loop; each weight is one fma and the hardware exp2, and the packed bf16
+// weights trade one pair of words between lane halves to reach the value
+// MFMA's key order.
 #include "mla_internal.hpp"
 
 namespace mla {
@@ -32,15 +34,9 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-#ifndef PREFILL_NQB
-#define PREFILL_NQB 1          // 32-query MFMA blocks per wave
-#endif
-#ifndef PREFILL_NW
-#define PREFILL_NW 4           // waves per workgroup
-#endif
-#ifndef PREFILL_NBUF
-#define PREFILL_NBUF 4         // tile buffers in the copy ring
-#endif
+constexpr int PF_NQB = 1;    // 32-query MFMA blocks per wave (two do not fit in registers without spills)
+constexpr int PF_NW = 4;     // waves per workgroup
+constexpr int PF_NBUF = 4;   // tile buffers in the copy ring
 constexpr int KT = 32;         // keys per tile
 constexpr int DH = 128, DR = 64, DV = 128;
 constexpr int DQ = DH + DR;    // query / key width
@@ -68,16 +64,6 @@ __device__ __forceinline__ long long vt_col(const PrefillArgs& a, int b, int u) 
   if (a.block_table == nullptr) return static_cast<long long>(b) * a.vt_seq + u;
   return store_row(a, b, u);
 }
-template <bool PAGED>
-__device__ __forceinline__ long long store_row_t(const PrefillArgs& a, int b, int u, int bs_log2) {
-  if constexpr (!PAGED) {
-    return static_cast<long long>(b) * a.capacity + u;
-  } else {
-    const int blk = a.block_table[b * a.max_blocks + (u >> bs_log2)];
-    return (static_cast<long long>(blk) << bs_log2) + (u & ((1 << bs_log2) - 1));
-  }
-}
-
 // LDS-DMA: each lane moves 16 bytes from its address to LDS at lds + 16 *
 // lane. Inline asm so that the compiler adds none of its own waits; the
 // kernel waits for the copies (vmcnt(0)) before the barrier that publishes
@@ -520,7 +506,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
   if (a.dtype != MLA_BF16 || a.d_h != DH || a.d_R != DR || a.d_v != DV) return hipErrorInvalidValue;
   if (a.block_table && (a.block_size < 8 || (a.block_size & (a.block_size - 1)))) return hipErrorInvalidValue;
   if (a.vt_ld % 8 || a.vt_seq % 8 || (a.d_c + a.d_R) % 8) return hipErrorInvalidValue;
-  constexpr int NQB = PREFILL_NQB, NW = PREFILL_NW, NBUF = PREFILL_NBUF;
+  constexpr int NQB = PF_NQB, NW = PF_NW, NBUF = PF_NBUF;
   constexpr int QT = NW * 32 * NQB;
   const long long blocks = static_cast<long long>(a.B) * a.H * ((a.T + QT - 1) / QT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
