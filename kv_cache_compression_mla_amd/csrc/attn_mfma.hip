@@ -474,7 +474,7 @@ void attn_mfma_kernel(Params p) {
     for (int s = 0; s < QK_STEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
-  // O^T accumulators: block (c, hb) holds columns of value block 4w + c
+  // O^T accumulators: block NW*c + hb holds columns of value block 4w + c
   // against heads 32hb..32hb+31.
   const bf16x8 zero8 = {};
   f32x16 oacc[4 * NW];
@@ -567,7 +567,7 @@ void attn_mfma_kernel(Params p) {
 #pragma unroll
       for (int hb = 0; hb < NW; ++hb) {
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                     : "+a"(oacc[4 * c + hb]) : "v"(cur), "v"(P[hb]));
+                     : "+a"(oacc[NW * c + hb]) : "v"(cur), "v"(P[hb]));
         if (vi == 3) P[hb] = p_operand(hb, 1);   // last use of the first k-step's weights
         between(step++);
       }
@@ -775,7 +775,7 @@ void attn_mfma_kernel(Params p) {
           float x[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[4 * c + hb][r]));
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[NW * c + hb][r]));
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int col = colbase(4 * w + c) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);

@@ -135,6 +135,17 @@ def test_v3_latent_norm_variant():
     check_step(inp, st, label="v3_gamma")
 
 
+@pytest.mark.parametrize("H", [32, 64, 96])
+def test_mfma_kernel_fewer_heads(H):
+    """The MFMA attention kernel with 1, 2 and 3 head blocks (its epilogue
+    stages 64 heads per round, so 96 heads end on a half round), on a ragged
+    batch with one sequence cut into several chunks."""
+    cfg = V3.with_(name=f"v3_h{H}", H=H, B=3, ctx=(40, 700, 2500), seed=13)
+    inp, st = run_step(cfg)
+    assert mla.decode_kernel(st.dims) == 1
+    check_step(inp, st, unabsorbed=False, label=f"H={H}")
+
+
 def test_generic_kernel_bf16_other_geometry():
     cfg = V3.with_(name="v3_h16", H=16, d=1024, d_cq=256, B=2, ctx=(5, 150))
     inp, st = run_step(cfg, num_splits=2)

@@ -95,6 +95,18 @@ def test_prefill_v3_small_ragged(algo, paged):
     check(pf, weights64(inp), f"v3 small {algo} paged={paged}")
 
 
+@pytest.mark.parametrize("bs", [8, 64])
+def test_prefill_materialised_page_sizes(bs):
+    """The MFMA prefill kernel's per-tile block lookups: 8-row blocks (four
+    per 32-key tile) and 64-row blocks (a tile inside one block)."""
+    cfg = V3.with_(name=f"v3_prefill_pages{bs}", B=2, ctx=(333, 90), paged=True, block_size=bs)
+    inp = make_inputs(cfg)
+    pf = DevicePrefill(inp, 70)
+    say(f"prefill v3 materialised {bs}-row pages")
+    run(pf, "materialised")
+    check(pf, weights64(inp), f"v3 pages{bs} materialised")
+
+
 @pytest.mark.parametrize("algo", list(ALGOS))
 def test_prefill_v3_two_query_tiles(algo):
     """130 tokens over 1000 rows: two 128-token tiles, the second with 2."""
