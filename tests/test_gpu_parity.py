@@ -146,6 +146,37 @@ def test_mfma_kernel_fewer_heads(H):
     check_step(inp, st, unabsorbed=False, label=f"H={H}")
 
 
+def test_batch_above_128_rows_per_product():
+    """160 sequences: every projection has more than 128 activation rows and
+    runs on the tiled GEMM (the streaming kernel takes at most 128), the
+    latent and rotary products of the append run as two launches."""
+    cfg = V3.with_(name="v3_b160", B=160, ctx=None, ctx_range=(1, 60), seed=14)
+    inp, st = run_step(cfg)
+    seqs = [0, 1, 80, 159, int(np.argmax(inp.ctx))]
+    check_step(inp, st, seqs=seqs, unabsorbed=False, label="B=160")
+
+
+def test_no_query_low_rank_bf16():
+    """d_cq = 0 in bf16 at the V3 attention widths (32 heads): the query
+    projections read the hidden state directly."""
+    cfg = V3.with_(name="v3_nocq", H=32, d=1024, d_cq=0, B=2, ctx=(33, 300), seed=15)
+    inp, st = run_step(cfg)
+    assert mla.decode_kernel(st.dims) == 1
+    check_step(inp, st, label="no_cq")
+
+
+def test_out_proj_per_head_outputs_only():
+    """mla_out_proj with W_O and out NULL stops after o_heads = W_UV(i) o_lat(i)."""
+    cfg = V3.with_(name="v3_oheads", B=3, ctx=(20, 90, 400), seed=16)
+    inp, st = run_step(cfg)
+    ref_heads = st.host(st.o_heads).copy()
+    st.o_heads.fill_(float("nan"))
+    mla.mla_out_proj(st.dims, st.o_lat, st.W["W_UV"], None, st.o_heads, None, st.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.host(st.o_heads), ref_heads)
+    check_step(inp, st, unabsorbed=True, label="o_heads")
+
+
 def test_generic_kernel_bf16_other_geometry():
     cfg = V3.with_(name="v3_h16", H=16, d=1024, d_cq=256, B=2, ctx=(5, 150))
     inp, st = run_step(cfg, num_splits=2)
