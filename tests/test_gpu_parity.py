@@ -251,7 +251,7 @@ def fill_append_slots(inp):
     rng = np.random.default_rng(1234)
     for b in range(inp.cfg.B):
         v = (rng.standard_normal(inp.cfg.D) * 1.7).astype(np.float32)
-        inp.row(b, int(inp.ctx[b]))[:] = gen.f32_to_bf16_bits(v)
+        inp.row(b, int(inp.ctx[b]))[:] = gen.f32_to_bf16_bits(v) if inp.cfg.dtype == "bf16" else v
 
 
 def attention_only(inp, q_bits, num_splits):
@@ -385,6 +385,55 @@ def test_sparse_attention_against_oracle(paged):
             if n == 1:   # one listed row: its latent, exactly
                 row = rows[lists[b, 0], :cfg.d_c]
                 assert np.array_equal(o_lat[b], np.broadcast_to(row, o_lat[b].shape)), (splits, b)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_sparse_attention_generic_kernel(paged):
+    """Sparse attention on the plain kernel (fp32, tiny geometry), contiguous
+    and 4-row pages, lists in random order with an empty one."""
+    cfg = gen.CONFIGS["tiny_fp32"].with_(name="tiny_sparse", B=3, ctx=(64, 10, 30), paged=paged, block_size=4,
+                                          seed=24)
+    inp = make_inputs(cfg)
+    q = gen.make_query(cfg)
+    fill_append_slots(inp)
+    lists, counts = gen.make_topk_indices(cfg, inp.seq_lens, 16)
+    counts[1] = 0
+    q64 = gen.to_f64(q, cfg.dtype)
+    for splits in (0, 2):
+        st = sparse_only(inp, q, lists, counts, splits)
+        assert mla.decode_kernel(st.dims) == 2
+        o_lat, lse = st.host(st.o_lat), st.host(st.lse)
+        for b in range(cfg.B):
+            n = int(counts[b])
+            if n == 0:
+                assert not o_lat[b].any() and np.all(np.isneginf(lse[b])), (splits, b)
+                continue
+            rows = gen.to_f64(inp.rows(b, int(inp.seq_lens[b])), cfg.dtype)
+            ref_o, ref_l = om.attend_sparse(q64[b, :, :cfg.d_c], q64[b, :, cfg.d_c:], rows, lists[b, :n], cfg.scale)
+            e_o = rel_err(o_lat[b], ref_o)
+            e_l = np.abs(lse[b] - ref_l).max() / max(np.abs(ref_l).max(), 1.0)
+            say(f"sparse generic paged={paged} s={splits} b={b} n={n} o_lat {e_o:.2e} lse {e_l:.2e}")
+            assert e_o <= tol(cfg) and e_l <= tol(cfg), (splits, b, e_o, e_l)
+
+
+def test_all_sequences_empty():
+    """Every sequence of the batch empty (max_seq_len 0), on the MFMA kernel
+    and on the plain one: zeros and lse = -inf everywhere."""
+    from kv_cache_compression_mla_amd.step import to_device
+    for cfg in (V3.with_(name="v3_all_empty", B=3, ctx=(10, 20, 30), seed=25),
+                gen.CONFIGS["tiny_fp32"].with_(name="tiny_all_empty", B=2, ctx=(5, 9))):
+        inp = make_inputs(cfg)
+        q = gen.make_query(cfg)
+        for splits in (0, 2):
+            st = DeviceStep(inp, num_splits=splits)
+            st.seq_lens.zero_()
+            st.o_lat.fill_(float("nan"))
+            st.lse.fill_(0.0)
+            mla.mla_decode_attn(st.dims, to_device(q, cfg.dtype), st.cdesc, st.seq_lens, 0, st.o_lat, st.lse,
+                                st.ws, splits)
+            torch.cuda.synchronize()
+            say(f"all empty {cfg.name} splits={splits}")
+            assert not st.host(st.o_lat).any() and np.all(np.isneginf(st.host(st.lse))), (cfg.name, splits)
 
 
 def test_sparse_full_list_equals_dense_bitwise():
