@@ -377,6 +377,38 @@ __device__ __forceinline__ void copy_part(const TileCopy& c, int k, uint32_t lat
   }
 }
 
+// Copy k (0..8) of this wave's share of an interior tile (all 32 rows before
+// row_end) in CONTIG or PAGED8 mode: the wave's 8-row group starts at `group`
+// (one contiguous run of rows), latent row k at group + k rows goes to LDS
+// lat + k * LROW, the rotary block (per-lane offset rope_voff from group) to
+// rope. No clamping and no table read per copy: one 64-bit scalar add and
+// the M0 update.
+template <int K>
+__device__ __forceinline__ void copy_interior(const uint16_t* group, uint32_t lane_off, uint32_t rope_voff,
+                                              uint32_t lat, uint32_t rope) {
+  if constexpr (K < 8) {
+    asm volatile("s_add_i32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3 offset:0"
+                 :: "s"(lat), "i"(K * LROW), "v"(lane_off), "s"(group + K * DW));
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:0"
+                 :: "s"(rope), "v"(rope_voff), "s"(group));
+  }
+}
+__device__ __forceinline__ void copy_interior_k(int k, const uint16_t* group, uint32_t lane_off,
+                                                uint32_t rope_voff, uint32_t lat, uint32_t rope) {
+  switch (k) {   // k is a constant after unrolling: one case survives
+    case 0: copy_interior<0>(group, lane_off, rope_voff, lat, rope); break;
+    case 1: copy_interior<1>(group, lane_off, rope_voff, lat, rope); break;
+    case 2: copy_interior<2>(group, lane_off, rope_voff, lat, rope); break;
+    case 3: copy_interior<3>(group, lane_off, rope_voff, lat, rope); break;
+    case 4: copy_interior<4>(group, lane_off, rope_voff, lat, rope); break;
+    case 5: copy_interior<5>(group, lane_off, rope_voff, lat, rope); break;
+    case 6: copy_interior<6>(group, lane_off, rope_voff, lat, rope); break;
+    case 7: copy_interior<7>(group, lane_off, rope_voff, lat, rope); break;
+    default: copy_interior<8>(group, lane_off, rope_voff, lat, rope); break;
+  }
+}
+
 // Workgroup barrier; this wave's LDS writes (the softmax weights) complete
 // first, so that every wave reads them after the barrier.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -664,6 +696,30 @@ void attn_mfma_kernel(Params p) {
     // still fly), every wave has written the weights of tile t and is past
     // tile t-1, whose stages tile t+3 reuses.
     int t = 0;
+    if constexpr (!per_row(PM)) {
+      // Steady state (t + 4 < ntiles): tiles t+1 and t+3 are interior (32
+      // rows before row_end), so no row is masked and the copies of tile t+3
+      // need no clamping; the general loop below takes the last iterations.
+      const int jr = lane >> 3;
+      const uint32_t rope_voff = jr * ROW_BYTES + 2 * DC + 16 * ((lane & 7) ^ rope_sw(8 * w + jr));
+      for (; t + 4 < ntiles; ++t) {
+        wait_vmcnt<DMA_PER_WAVE>();
+        block_barrier();
+        const uint16_t* group = row_ptr<PM>(p, bc, tile_r0(t + 3) + 8 * w);
+        const uint32_t lat3 = smem_lds + lat_off(t + 3) + 8 * w * LROW;
+        const uint32_t rope3 = smem_lds + rope_off(t + 3) + w * 1024;
+        Soft N;
+        qk(t + 1, N.x, [&](int s) {
+          if (s % 4 == 1 && s / 4 < DMA_PER_WAVE) copy_interior_k(s / 4, group, lane_off, rope_voff, lat3, rope3);
+        });
+        const int pb_next = p_off(t + 1);
+        pv(t, [&](int step) {
+          if (step < SM_STEPS) soft_step(N, step, TILE, false, grew, pb_next);
+        });
+#pragma unroll
+        for (int k = PV_STEPS; k < SM_STEPS; ++k) soft_step(N, k, TILE, false, grew, pb_next);
+      }
+    }
     for (; t + 1 < ntiles; ++t) {
       if (t + 2 < ntiles) wait_vmcnt<DMA_PER_WAVE>();
       else wait_vmcnt<0>();
