@@ -442,9 +442,9 @@ __global__ __launch_bounds__(GTH) void gemm_stream_kernel(GemmP p) {
 // ---------------------------------------------------------------------------
 constexpr int TT_N = 128, TT_M = 128;
 constexpr int TT_WB = TT_N * 128, TT_AB = TT_M * 128;     // bytes per stage
-constexpr int TT_STAGE = TT_WB + TT_AB;                   // 48 KiB
+constexpr int TT_STAGE = TT_WB + TT_AB;                   // 32 KiB
 constexpr int TT_NS = 2;
-constexpr int TT_PW = TT_STAGE / 1024 / 4;                 // copies per wave per stage: 12
+constexpr int TT_PW = TT_STAGE / 1024 / 4;                 // copies per wave per stage: 8
 constexpr int TT_OROW = TT_N * 2 + 16;                    // staged output row stride (bytes)
 static_assert(TT_M * TT_OROW <= TT_NS * TT_STAGE, "output tile fits in the ring");
 
