@@ -194,6 +194,26 @@ def prefill_sweep(Ts, steps, warmup):
         torch.cuda.empty_cache()
 
 
+def measured_copy_gbps(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate of this GPU (bytes read + written per
+    second), the practical counterpart of the published HBM peak."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +298,7 @@ def main():
     calls_ms = {c: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evc])), 5)
                 for i, c in enumerate(calls)}
 
+    copy_gbps = measured_copy_gbps(torch)
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     cache_gbps = cache_bytes / (attn_ms * 1e-3) / 1e9
     achieved_gbps = attn_bytes / (attn_ms * 1e-3) / 1e9
@@ -308,6 +329,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "kernel": "mla_decode_attn call (attn_mfma_kernel + combine_chunks)",
+                     "measured_copy_GBps": round(copy_gbps, 1),
+                     "frac_of_copy": round(achieved_gbps / copy_gbps, 4),
                      "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:
