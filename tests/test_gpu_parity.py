@@ -129,6 +129,21 @@ def test_v3_small_paged(bs):
     check_step(inp, st, label=f"v3_paged bs={bs}")
 
 
+@pytest.mark.parametrize("bs", [0, 16])
+def test_steady_loop_boundaries(bs):
+    """One chunk per sequence (num_splits = 1) with 4 to 7 tiles, full and
+    ragged last tiles: the attention kernel's steady-state loop (which runs
+    while the tile being scored and the tile being copied are both whole)
+    hands over to the general loop at every offset from the chunk end, in
+    the contiguous and the paged (16-row pages) addressing modes."""
+    ctx = (127, 128, 159, 160, 191, 222)          # attended rows 128, 129, 160, 161, 192, 223
+    cfg = V3.with_(name="v3_steady", B=len(ctx), ctx=ctx, seed=21,
+                   **({"paged": True, "block_size": bs} if bs else {}))
+    inp, st = run_step(cfg, num_splits=1)
+    assert mla.decode_kernel(st.dims) == 1
+    check_step(inp, st, unabsorbed=False, label=f"steady bs={bs}")
+
+
 def test_v3_latent_norm_variant():
     cfg = V3.with_(name="v3_gamma", B=2, ctx=(10, 77), gamma=True, seed=6)
     inp, st = run_step(cfg)
