@@ -84,6 +84,24 @@ def test_rope_two_dimensional_case_is_plain_rotation():
                                    [-math.sin(pos), math.cos(pos)], atol=1e-15)
 
 
+def test_rope_equals_complex_multiplication():
+    # The rotary form written as complex arithmetic: pair j is the complex
+    # number x[2j] + i x[2j+1], multiplied by exp(i * pos * theta^(-2j/d)).
+    # A different route to the same numbers (numpy complex exp and product,
+    # no cos/sin pair formula), so a swapped pair order, a sign flip or a
+    # wrong frequency index fails here for every pair, not only for d = 2.
+    rng = np.random.default_rng(5)
+    for d, theta in ((64, 10000.0), (8, 10000.0), (16, 500.0)):
+        x = rng.standard_normal((5, d))
+        z = x[:, 0::2] + 1j * x[:, 1::2]
+        freq = theta ** (-np.arange(0, d, 2) / d)
+        for pos in (1, 3, 1000, 32768):
+            w = z * np.exp(1j * pos * freq)
+            ref = np.empty_like(x)
+            ref[:, 0::2], ref[:, 1::2] = w.real, w.imag
+            np.testing.assert_allclose(om.rope(x, pos, theta), ref, rtol=0, atol=1e-10)
+
+
 def test_rope_relative_position_property():
     # (R_m q) . (R_n k) depends on n - m only.
     rng = np.random.default_rng(4)
