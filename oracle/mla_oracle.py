@@ -24,7 +24,10 @@ Readings of points the pages leave open:
     flow": append, then attend over all history).
   * Rotary embedding: consecutive pairs (x[2j], x[2j+1]) rotated by angle
     pos * theta^(-2j/d_R) (the original rotary form; the pages fix only that
-    a position dependent rotation is applied, [DONG] section 4).
+    a position dependent rotation is applied, [DONG] section 4). Parity
+    unpinned on this choice of convention: no page fixes it. Within it, the
+    tests pin rope() by its complex-multiplication form, its identities and
+    the relative-position property.
   * The cache stores the already rotated rotary key ([KB] section 3 sketch marks
     the rotated key as the cached object; [DONG] B2 says it is already rotated
     when heads use it).
