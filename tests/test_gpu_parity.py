@@ -240,6 +240,28 @@ def test_splits_are_an_exact_reformulation_and_deterministic():
         assert e_split <= 1e-2 and e_ref <= 1e-2 and e_lse <= 1e-4, s
 
 
+def test_more_than_64_chunks_per_sequence():
+    """One sequence of 32768 rows: the balanced plan cuts it into 128 chunks,
+    more than the 64 whose (m, l) the combine reads one per lane, so the
+    combine takes its sequential path. Against the oracle, and against 8
+    chunks (the per-lane path) to the bf16 bar."""
+    cfg = V3.with_(name="v3_long1", B=1, ctx=(32767,), seed=22)
+    inp = make_inputs(cfg)
+    st = DeviceStep(inp, num_splits=0, ws_splits=(8,))
+    say(f"v3_long1 splits={st.splits}")
+    assert st.splits > 64
+    st.run()
+    torch.cuda.synchronize()
+    o_auto, lse_auto = st.host(st.o_lat).copy(), st.host(st.lse).copy()
+    check_step(inp, st, unabsorbed=False, label="128 chunks")
+    st.decode_attn(num_splits=8)
+    torch.cuda.synchronize()
+    e = rel_err(o_auto, st.host(st.o_lat))
+    e_lse = np.abs(lse_auto - st.host(st.lse)).max() / np.abs(lse_auto).max()
+    say(f"128 vs 8 chunks: o_lat {e:.2e} lse {e_lse:.2e}")
+    assert e <= 1e-2 and e_lse <= 1e-4
+
+
 def test_paged_equals_contiguous_bitwise():
     base = V3.with_(name="v3_cmp", B=3, ctx=(90, 300, 640), seed=12)
     inp_c = make_inputs(base)
