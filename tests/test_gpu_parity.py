@@ -122,7 +122,7 @@ def test_v3_small_contiguous(ctx, splits):
     check_step(inp, st, label=f"v3_small{ctx}")
 
 
-@pytest.mark.parametrize("bs", [64, 16, 128])
+@pytest.mark.parametrize("bs", [64, 16, 128, 8, 4, 1])
 def test_v3_small_paged(bs):
     cfg = V3.with_(name="v3_paged", B=3, ctx=(63, 64, 200), paged=True, block_size=bs, seed=4)
     inp, st = run_step(cfg, num_splits=2)
