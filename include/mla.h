@@ -290,11 +290,17 @@ mla_status mla_out_proj_precomposed(const mla_dims* dims, int32_t B, const float
  *          bytes. The materialised form expands every row the cache stores
  *          (contiguous: B * capacity, paged: n_blocks * block_size) into it:
  *          (d_h + d_v) * H elements per row.
+ * MLA_PREFILL_AUTO takes the form a cost model expects to be faster. The model
+ * is fitted to measurements on MI355X at the DeepSeek-V3 widths. It picks the
+ * absorbed form while the attended rows, bounded from T and max_seq_len, stay
+ * below 320 per stored row, and the materialised form above that. A form with
+ * no kernel for the shape yields to the other. mla_prefill_choose reports
+ * the choice; mla_prefill_workspace_bytes with MLA_PREFILL_AUTO sizes it.
  * Errors: MLA_ERR_SHAPE for B, T <= 0, an unknown algo or max_seq_len above
  * the cache; MLA_ERR_UNSUPPORTED if B * T exceeds 32768 (absorbed, V3
  * geometry) or the cache stores more than 8,388,480 rows (materialised).
  */
-typedef enum { MLA_PREFILL_MATERIALIZED = 0, MLA_PREFILL_ABSORBED = 1 } mla_prefill_algo;
+typedef enum { MLA_PREFILL_MATERIALIZED = 0, MLA_PREFILL_ABSORBED = 1, MLA_PREFILL_AUTO = 2 } mla_prefill_algo;
 
 mla_status mla_prefill_attn(const mla_dims* dims, int32_t B, int32_t T, const void* q,
                             const mla_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
@@ -304,6 +310,12 @@ mla_status mla_prefill_attn(const mla_dims* dims, int32_t B, int32_t T, const vo
 /* Workspace bytes mla_prefill_attn needs; 0 on bad arguments. */
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t B, int32_t T, int32_t max_seq_len,
                                    const mla_cache* cache, int32_t algo);
+
+/* The form MLA_PREFILL_AUTO runs for these arguments (MLA_PREFILL_MATERIALIZED
+ * or MLA_PREFILL_ABSORBED); -1 on bad arguments or when neither form has a
+ * kernel for the shape. Host only: reads the structs, no device memory. */
+int32_t mla_prefill_choose(const mla_dims* dims, int32_t B, int32_t T, int32_t max_seq_len,
+                           const mla_cache* cache);
 
 /* Workspace bytes that suffice for every call above except mla_prefill_attn, with these sizes
  * (num_splits as passed to mla_decode_attn, 0 = automatic). 0 on bad dims. */

@@ -534,26 +534,54 @@ PrefillPlan prefill_plan(const mla_dims* d, int B, int T, int max_seq_len, const
 
 constexpr long long kMaxPrefillRows = 65535LL * 128;   // rows one expansion product takes (128 per z block)
 
-mla_status check_prefill_sizes(const mla_dims* d, int B, int T, int max_seq_len, const mla_cache* c, int algo) {
+// Why a validated shape has no kernel in this form, or NULL when it has one.
+const char* prefill_unfit(const mla_dims* d, int B, int T, const mla_cache* c, int algo) {
+  if (algo == MLA_PREFILL_MATERIALIZED) {
+    if (cache_store_rows(c, B) > kMaxPrefillRows || static_cast<long long>(d->H) * d->d_v > kMaxPrefillRows)
+      return "prefill: cache too large to expand in one product";
+    if (!prefill_mfma(d, c) && d->d_v > 1024) return "prefill: d_v above 1024";
+  } else {
+    const long long BT = static_cast<long long>(B) * T;
+    static_assert(kMaxMfmaBatch == 32768, "the message below names the limit");
+    if (mfma_attn(d) && BT > kMaxMfmaBatch) return "prefill (absorbed): B * T above 32768";
+    if (BT > kMaxPrefillRows) return "prefill: B * T too large";
+  }
+  return nullptr;
+}
+
+// MLA_PREFILL_AUTO. Costs fitted to the prefill sweep on MI355X (V3 widths,
+// 4 sequences of 4096 rows, T = 1 .. 1024): the absorbed form costs about
+// 0.33 ns per attended row (row, token) and the materialised form 0.10 ns
+// per attended row plus 73 ns per stored row (the expansion), so the
+// absorbed form is the faster one while the attended rows stay below about
+// 320 per stored row. Attended rows are bounded from T and max_seq_len (every
+// sequence taken at max_seq_len); a form with no kernel for the shape yields
+// to the other.
+constexpr double kPrefillAutoRatio = 320.0;
+int resolve_prefill_algo(const mla_dims* d, int B, int T, int max_seq_len, const mla_cache* c) {
+  const double L = max_seq_len, t = T;
+  const double per_seq = T <= max_seq_len ? t * L - t * (t - 1.0) / 2.0 : L * (L + 1.0) / 2.0;
+  const double attended = static_cast<double>(B) * per_seq;
+  const double stored = static_cast<double>(cache_store_rows(c, B));
+  int pick = attended < kPrefillAutoRatio * stored ? MLA_PREFILL_ABSORBED : MLA_PREFILL_MATERIALIZED;
+  if (prefill_unfit(d, B, T, c, pick))
+    pick = pick == MLA_PREFILL_ABSORBED ? MLA_PREFILL_MATERIALIZED : MLA_PREFILL_ABSORBED;
+  return pick;
+}
+
+// Validates the arguments and resolves MLA_PREFILL_AUTO in *algo.
+mla_status check_prefill_sizes(const mla_dims* d, int B, int T, int max_seq_len, const mla_cache* c, int* algo) {
   if (B <= 0 || T <= 0) return fail(MLA_ERR_SHAPE, "prefill: B and T must be positive");
   if (max_seq_len < 0) return fail(MLA_ERR_SHAPE, "prefill: negative max_seq_len");
-  if (algo != MLA_PREFILL_MATERIALIZED && algo != MLA_PREFILL_ABSORBED)
-    return fail(MLA_ERR_SHAPE, "prefill: unknown algorithm %d", algo);
+  if (*algo != MLA_PREFILL_MATERIALIZED && *algo != MLA_PREFILL_ABSORBED && *algo != MLA_PREFILL_AUTO)
+    return fail(MLA_ERR_SHAPE, "prefill: unknown algorithm %d", *algo);
   MLA_TRY(check_cache(d, c));
   if (!c->block_table && max_seq_len > c->capacity)
     return fail(MLA_ERR_SHAPE, "max_seq_len %d exceeds capacity %d", max_seq_len, c->capacity);
   if (c->block_table && static_cast<long long>(max_seq_len) > static_cast<long long>(c->max_blocks) * c->block_size)
     return fail(MLA_ERR_SHAPE, "max_seq_len exceeds max_blocks * block_size");
-  if (algo == MLA_PREFILL_MATERIALIZED) {
-    if (cache_store_rows(c, B) > kMaxPrefillRows || static_cast<long long>(d->H) * d->d_v > kMaxPrefillRows)
-      return fail(MLA_ERR_UNSUPPORTED, "prefill: cache too large to expand in one product");
-    if (!prefill_mfma(d, c) && d->d_v > 1024) return fail(MLA_ERR_UNSUPPORTED, "prefill: d_v above 1024");
-  } else {
-    const long long BT = static_cast<long long>(B) * T;
-    if (mfma_attn(d) && BT > kMaxMfmaBatch)
-      return fail(MLA_ERR_UNSUPPORTED, "prefill (absorbed): B * T above %d", kMaxMfmaBatch);
-    if (BT > kMaxPrefillRows) return fail(MLA_ERR_UNSUPPORTED, "prefill: B * T too large");
-  }
+  if (*algo == MLA_PREFILL_AUTO) *algo = resolve_prefill_algo(d, B, T, max_seq_len, c);
+  if (const char* why = prefill_unfit(d, B, T, c, *algo)) return fail(MLA_ERR_UNSUPPORTED, "%s", why);
   return MLA_OK;
 }
 
@@ -661,8 +689,16 @@ extern "C" {
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t B, int32_t T, int32_t max_seq_len,
                                    const mla_cache* cache, int32_t algo) {
   if (check_dims(dims) != MLA_OK || !cache) return 0;
-  if (check_prefill_sizes(dims, B, T, max_seq_len, cache, algo) != MLA_OK) return 0;
+  if (check_prefill_sizes(dims, B, T, max_seq_len, cache, &algo) != MLA_OK) return 0;
   return prefill_plan(dims, B, T, max_seq_len, cache, algo).total();
+}
+
+int32_t mla_prefill_choose(const mla_dims* dims, int32_t B, int32_t T, int32_t max_seq_len,
+                           const mla_cache* cache) {
+  if (check_dims(dims) != MLA_OK || !cache) return -1;
+  int32_t algo = MLA_PREFILL_AUTO;
+  if (check_prefill_sizes(dims, B, T, max_seq_len, cache, &algo) != MLA_OK) return -1;
+  return algo;
 }
 
 mla_status mla_prefill_attn(const mla_dims* dims, int32_t B, int32_t T, const void* q, const mla_cache* cache,
@@ -670,7 +706,7 @@ mla_status mla_prefill_attn(const mla_dims* dims, int32_t B, int32_t T, const vo
                             int32_t algo, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
   MLA_TRY(check_dims(dims));
   if (!q || !cache || !seq_lens || !W_UK || !W_UV || !o || !ws) return fail(MLA_ERR_NULL, "prefill: NULL pointer");
-  MLA_TRY(check_prefill_sizes(dims, B, T, max_seq_len, cache, algo));
+  MLA_TRY(check_prefill_sizes(dims, B, T, max_seq_len, cache, &algo));
   for (const void* p : {q, static_cast<const void*>(seq_lens), W_UK, W_UV, static_cast<const void*>(o),
                         static_cast<const void*>(ws)})
     if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "prefill: pointer not 16-byte aligned");

@@ -65,6 +65,8 @@ _SIGS = {
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.POINTER(MLACache), ctypes.c_int32]),
+    "mla_prefill_choose": (ctypes.c_int32, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.POINTER(MLACache)]),
     "mla_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32]),
     "mla_decode_num_splits": (ctypes.c_int32, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int32,
@@ -229,7 +231,12 @@ def mla_out_proj_precomposed(dims, o_lat, W_OV, out, ws, stream=None):
         _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)), "mla_out_proj_precomposed")
 
 
-PREFILL_MATERIALIZED, PREFILL_ABSORBED = 0, 1
+PREFILL_MATERIALIZED, PREFILL_ABSORBED, PREFILL_AUTO = 0, 1, 2
+
+
+def prefill_choose(dims: MLADims, B: int, T: int, max_seq_len: int, cache: MLACache) -> int:
+    """The form PREFILL_AUTO runs for these sizes (-1 on bad arguments)."""
+    return lib().mla_prefill_choose(ctypes.byref(dims), B, T, max_seq_len, ctypes.byref(cache))
 
 
 def prefill_workspace_bytes(dims: MLADims, B: int, T: int, max_seq_len: int, cache: MLACache, algo: int) -> int:

@@ -182,3 +182,28 @@ def test_prefill_argument_errors(L):
     assert f(B=64, T=1024, algo=ABS, wsb=1 << 40) == UNSUPPORTED
     assert L.mla_prefill_workspace_bytes(ctypes.byref(d), 64, 1024, 4096, ctypes.byref(c), ABS) == 0
     assert L.mla_prefill_workspace_bytes(ctypes.byref(d), 4, 0, 4096, ctypes.byref(c), MAT) == 0
+
+
+def test_prefill_auto_choice(L):
+    # The cost model's choice on the swept shape (4 sequences of 4096 rows in a
+    # 4097-row cache): absorbed up to 256 new tokens, materialised from 512.
+    d = v3()
+    c = mla.MLACache(A, None, 4097, 0, 0, 0)
+    MAT, ABS, AUTO = mla.PREFILL_MATERIALIZED, mla.PREFILL_ABSORBED, mla.PREFILL_AUTO
+    choose = lambda B, T, msl=4096, cache=c: L.mla_prefill_choose(ctypes.byref(d), B, T, msl, ctypes.byref(cache))
+    assert [choose(4, T) for T in (1, 64, 256)] == [ABS] * 3
+    assert [choose(4, T) for T in (512, 1024, 4096)] == [MAT] * 3
+    # B * T above the absorbed kernel's 32768 token entries: materialised
+    assert choose(64, 600, 4096, mla.MLACache(A, None, 4097, 0, 0, 0)) == MAT
+    # a pool too large to expand in one product (8,960,000 stored rows):
+    # absorbed, although at 8192 tokens of 131072-row sequences (464 attended
+    # rows per stored row) the model prices the materialised form lower
+    big = mla.MLACache(A, A, 0, 64, 2048, 140000)
+    assert choose(4, 8192, 131072, big) == ABS
+    # bad arguments
+    assert choose(0, 8) == -1 and choose(4, 8, 5000) == -1
+    # the workspace for AUTO is the chosen form's
+    for T in (64, 1024):
+        pick = choose(4, T)
+        assert L.mla_prefill_workspace_bytes(ctypes.byref(d), 4, T, 4096, ctypes.byref(c), AUTO) == \
+            L.mla_prefill_workspace_bytes(ctypes.byref(d), 4, T, 4096, ctypes.byref(c), pick)

@@ -156,3 +156,25 @@ def test_prefill_full_size_sampled():
     el = np.abs(lm - la).max() / np.abs(la).max()
     say(f"materialised vs absorbed: o {e:.2e} lse {el:.2e}")
     assert e <= 1e-2 and el <= 1e-2
+
+
+@pytest.mark.parametrize("T", [8, 512])
+def test_auto_runs_the_chosen_form(T):
+    """MLA_PREFILL_AUTO gives, bit for bit, the output of the form
+    mla_prefill_choose reports: the absorbed one for 8 new tokens of 1024-row
+    sequences, the materialised one for 512."""
+    cfg = V3.with_(name=f"v3_prefill_auto{T}", B=2, ctx=(1024, 1000), seed=31)
+    inp = make_inputs(cfg)
+    pf = DevicePrefill(inp, T)
+    pick = mla.prefill_choose(pf.dims, cfg.B, T, pf.max_seq_len, pf.cdesc)
+    say(f"T={T}: chosen form {pick}")
+    assert pick == (mla.PREFILL_ABSORBED if T == 8 else mla.PREFILL_MATERIALIZED)
+    pf.run(pick)
+    torch.cuda.synchronize()
+    o_pick, l_pick = pf.o.clone(), pf.lse.clone()
+    pf.o.fill_(float("nan"))
+    pf.lse.fill_(float("nan"))
+    pf.run(mla.PREFILL_AUTO)
+    torch.cuda.synchronize()
+    assert torch.equal(pf.o, o_pick) and torch.equal(pf.lse, l_pick)
+    check(pf, weights64(inp), f"auto T={T}", tokens=[0, T // 2, T - 1])
