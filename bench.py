@@ -189,6 +189,8 @@ def prefill_sweep(Ts, steps, warmup):
             res[name] = {"ms": round(ms, 4), "GFLOP": round(flops / 1e9, 2),
                          "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
         res["faster"] = min(("materialised", "absorbed"), key=lambda k: res[k]["ms"])
+        pick = mla.prefill_choose(pf.dims, cfg.B, T, pf.max_seq_len, pf.cdesc)
+        res["auto_picks"] = {mla.PREFILL_MATERIALIZED: "materialised", mla.PREFILL_ABSORBED: "absorbed"}.get(pick)
         print(json.dumps(res), flush=True)
         del pf
         torch.cuda.empty_cache()

@@ -293,7 +293,7 @@ mla_status mla_out_proj_precomposed(const mla_dims* dims, int32_t B, const float
  * MLA_PREFILL_AUTO takes the form a cost model expects to be faster. The model
  * is fitted to measurements on MI355X at the DeepSeek-V3 widths. It picks the
  * absorbed form while the attended rows, bounded from T and max_seq_len, stay
- * below 320 per stored row, and the materialised form above that. A form with
+ * below 360 per stored row, and the materialised form above that. A form with
  * no kernel for the shape yields to the other. mla_prefill_choose reports
  * the choice; mla_prefill_workspace_bytes with MLA_PREFILL_AUTO sizes it.
  * Errors: MLA_ERR_SHAPE for B, T <= 0, an unknown algo or max_seq_len above

@@ -551,13 +551,13 @@ const char* prefill_unfit(const mla_dims* d, int B, int T, const mla_cache* c, i
 
 // MLA_PREFILL_AUTO. Costs fitted to the prefill sweep on MI355X (V3 widths,
 // 4 sequences of 4096 rows, T = 1 .. 1024): the absorbed form costs about
-// 0.33 ns per attended row (row, token) and the materialised form 0.10 ns
-// per attended row plus 73 ns per stored row (the expansion), so the
-// absorbed form is the faster one while the attended rows stay below about
-// 320 per stored row. Attended rows are bounded from T and max_seq_len (every
-// sequence taken at max_seq_len); a form with no kernel for the shape yields
-// to the other.
-constexpr double kPrefillAutoRatio = 320.0;
+// 0.31-0.33 ns per attended row (row, token) and the materialised form
+// 0.10 ns per attended row plus 73 ns per stored row (the expansion). The
+// two forms cost the same at 340-385 attended rows per stored row on the
+// boxes measured; the absorbed form is taken below 360. Attended rows are
+// bounded from T and max_seq_len (every sequence taken at max_seq_len); a
+// form with no kernel for the shape yields to the other.
+constexpr double kPrefillAutoRatio = 360.0;
 int resolve_prefill_algo(const mla_dims* d, int B, int T, int max_seq_len, const mla_cache* c) {
   const double L = max_seq_len, t = T;
   const double per_seq = T <= max_seq_len ? t * L - t * (t - 1.0) / 2.0 : L * (L + 1.0) / 2.0;
