@@ -37,6 +37,26 @@ def _rotate_pairs(v, pos, theta):
     return out
 
 
+def brute_compress_row(h, W_DKV, W_KR, pos, theta, gamma=None, eps=1e-6):
+    """The new token's row [c ; k_R] before storage rounding, in loops.
+
+    c = W_DKV h; with a gain gamma the latent alone is RMS-normalised,
+    c_j * gamma_j / sqrt(mean_k c_k^2 + eps) ("Understanding MLA", Phase A,
+    step A2: the 512-wide latent is normalised and the 64-wide rotary key is
+    left alone; its section 5 table marks the rotary key as not normed).
+    k_R = RoPE(W_KR h, pos), never normalised.
+    """
+    c = _matvec(W_DKV, h)
+    if gamma is not None:
+        ms = 0.0
+        for v in c:
+            ms += v * v
+        ms /= len(c)
+        inv = 1.0 / math.sqrt(ms + eps)
+        c = [c[j] * float(gamma[j]) * inv for j in range(len(c))]
+    return c + _rotate_pairs(_matvec(W_KR, h), pos, theta)
+
+
 def brute_step(h, prior_rows, W, pos, theta, scale, round_fn):
     """Return (stored new row, per-head outputs o [H][d_v], out [d]).
 

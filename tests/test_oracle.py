@@ -138,6 +138,55 @@ def test_rms_norm_closed_forms():
     assert not np.allclose(W @ om.rms_norm(x, np.ones(512)), om.rms_norm(W @ x, np.ones(512)))
 
 
+@pytest.mark.parametrize("d,d_c,d_R,pos", [(64, 16, 8, 3), (256, 32, 8, 64), (512, 128, 64, 4097)])
+def test_compress_row_normalises_the_latent_only(d, d_c, d_R, pos):
+    """"Understanding MLA", Phase A, A2 normalises the latent and leaves the
+    rotary key alone (its section 5 table: the rotary key is not normed). With
+    a gain, the rotary part must equal the gain-free row's bit for bit, and
+    the latent part must equal c_j gamma_j / sqrt(mean(c^2) + eps) computed
+    in loops. A norm over the whole row, a dropped gain or eps, or a norm
+    applied to the rotary key fails here."""
+    rng = np.random.default_rng(d + pos)
+    h = rng.standard_normal(d)
+    W_DKV = 0.05 * rng.standard_normal((d_c, d))
+    W_KR = 0.05 * rng.standard_normal((d_R, d))
+    gamma = 1.0 + 0.3 * rng.standard_normal(d_c)
+    plain = om.compress_row(h, W_DKV, W_KR, pos, 10000.0)
+    normed = om.compress_row(h, W_DKV, W_KR, pos, 10000.0, gamma=gamma, eps=1e-6)
+    assert normed.shape == (d_c + d_R,)
+    np.testing.assert_array_equal(normed[d_c:], plain[d_c:])
+    ref = brute.brute_compress_row(h.tolist(), W_DKV.tolist(), W_KR.tolist(), pos, 10000.0,
+                                   gamma=gamma.tolist(), eps=1e-6)
+    np.testing.assert_allclose(normed, ref, rtol=1e-12, atol=1e-14)
+    # the gain-free latent is the plain down-projection, in loops too
+    ref0 = brute.brute_compress_row(h.tolist(), W_DKV.tolist(), W_KR.tolist(), pos, 10000.0)
+    np.testing.assert_allclose(plain, ref0, rtol=1e-12, atol=1e-14)
+    # closed form: with unit gain the normalised latent has RMS sqrt(ms / (ms + eps))
+    c = W_DKV @ h
+    ms = float(np.mean(c * c))
+    unit = om.compress_row(h, W_DKV, W_KR, pos, 10000.0, gamma=np.ones(d_c), eps=1e-6)
+    np.testing.assert_allclose(np.sqrt(np.mean(unit[:d_c] ** 2)), math.sqrt(ms / (ms + 1e-6)), rtol=1e-13)
+    # the rotary part of a normalised row is not of unit RMS in general (it is
+    # the plain rotated projection), which a whole-row norm would change
+    assert abs(np.sqrt(np.mean(normed[d_c:] ** 2)) - np.sqrt(np.mean(plain[d_c:] ** 2))) == 0.0
+
+
+def test_decode_step_with_gain_matches_brute_force_row():
+    """The stored row of a step with the latent norm equals the loop version
+    rounded to the storage dtype (the oracle's only rounding)."""
+    cfg = gen.CONFIGS["tiny_fp32"]
+    inp = make_inputs(cfg)
+    W = weights64(inp)
+    h = gen.to_f64(inp.h_t[0], cfg.dtype)
+    prior = gen.to_f64(inp.rows(0, int(inp.ctx[0])), cfg.dtype)
+    pos = int(inp.ctx[0])
+    gamma = 1.0 + 0.1 * np.random.default_rng(3).standard_normal(cfg.d_c)
+    ref = om.decode_step(h, prior, W, pos, cfg.theta, cfg.scale, "fp32", gamma=gamma)
+    row = brute.brute_compress_row(h.tolist(), W["W_DKV"].tolist(), W["W_KR"].tolist(), pos, cfg.theta,
+                                   gamma=gamma.tolist())
+    np.testing.assert_array_equal(ref["row"], np.array(row, dtype=np.float32).astype(np.float64))
+
+
 # --------------------------------------------------------------------------
 # Cache arithmetic printed on the pages
 # --------------------------------------------------------------------------
