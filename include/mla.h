@@ -37,7 +37,8 @@
  *    non-zero status means nothing was enqueued (except MLA_ERR_HIP, which
  *    reports a launch failure). Device faults surface at the caller's
  *    synchronisation. Device-side preconditions (positions below capacity,
- *    block-table entries inside the pool) are the caller's to keep.
+ *    block-table entries inside the pool, top-k entries inside a sequence)
+ *    are the caller's to keep; mla_check_indices checks host copies of them.
  *  - The calls are re-entrant; calls that share output or workspace buffers
  *    on different streams race.
  */
@@ -200,6 +201,39 @@ mla_status mla_decode_attn_sparse(const mla_dims* dims, int32_t B, const void* q
                                   float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mla_check_indices -- host-side check of the device-side preconditions.
+ * The kernels read positions, lengths, block-table entries and top-k lists
+ * from device memory without checking them (a check per element would sit
+ * in the hot loops); a violation reads or writes outside the cache. This
+ * call checks HOST copies of those arrays against the cache description.
+ * Any array may be NULL to skip its checks.
+ *   pos         [B] append positions (mla_compress_append, mla_absorb_q):
+ *               0 <= pos[b] < capacity (contiguous) or < max_blocks *
+ *               block_size with a valid block-table entry (paged); and no
+ *               two sequences append into the same cache slot (paged)
+ *   seq_lens    [B] rows attended (mla_decode_attn, mla_prefill_attn):
+ *               0 <= seq_lens[b] <= max_seq_len and <= capacity (contiguous)
+ *               or max_blocks * block_size (paged), every block-table entry
+ *               that covers rows [0, seq_lens[b]) valid
+ *   max_seq_len the host bound passed with seq_lens
+ *   block_table [B][max_blocks] host copy of cache->block_table; required
+ *               for a paged cache when any of pos, seq_lens, indices is given
+ *   indices     [B][topk] and counts [B] (mla_decode_attn_sparse): 0 <=
+ *               counts[b] <= topk, every listed position j < counts[b] a row
+ *               of the cache (as for pos) and, with seq_lens given, below
+ *               seq_lens[b]
+ * A valid block-table entry is 0 <= entry < n_blocks. Returns MLA_OK, or
+ * MLA_ERR_SHAPE with mla_last_error naming the first violation (array,
+ * sequence, value), MLA_ERR_NULL for a missing host block table or indices
+ * without counts; dims and cache are validated as by the other calls. Host
+ * only: reads host memory, touches no device memory, enqueues nothing.
+ */
+mla_status mla_check_indices(const mla_dims* dims, int32_t B, const mla_cache* cache,
+                             const int32_t* pos, const int32_t* seq_lens, int32_t max_seq_len,
+                             const int32_t* block_table, const int32_t* indices, int32_t topk,
+                             const int32_t* counts);
+
+/*
  * mla_out_proj -- back to the hidden width.
  *   o_heads(b,i) = W_UV(i) o_lat(b,i)       ([CASS] value projection after the
  *                                            weighted sum)
@@ -212,7 +246,8 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat,
                         void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Precomposed weights ([KB] section 3, "the core trick": the key
+ * Precomposed weights ([KB] section 2 "Derivation", paragraph "The RoPE
+ * obstruction": the key
  * up-projection folded into the query-side matrix once, offline; [CASS]
  * "absorbed-weights box": the value up-projection pre-multiplied into the
  * output projection). The per-head products are formed once:

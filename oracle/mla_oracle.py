@@ -316,8 +316,9 @@ def prefill_attend_absorbed(qC, qR, rows, pos, W_UK, W_UV, scale: float):
 def precompose_qk(W_UQ, W_UK) -> np.ndarray:
     """W_QK(i) = W_UK(i)^T W_UQ(i) in R^{d_c x qin}, per head.
 
-    [KB] section 3 ("the core trick"): the key up-projection is folded into
-    the query-side matrix once, offline, so the absorbed query comes from one
+    [KB] section 2 "Derivation", paragraph "The RoPE obstruction": the key
+    up-projection is folded into the query-side matrix once, offline (the
+    section 3 sketch repeats this as a comment), so the absorbed query comes from one
     product with c_Q. The printed composite W_UK W_UQ does not chain for
     W_UK in R^{d_h x d_c}; the transpose on W_UK is the reading (the same one
     absorb_q takes), which makes q_lat(i) = W_QK(i) c_Q = W_UK(i)^T q_C(i).
