@@ -6,6 +6,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
+#include <vector>
 
 #include "mla.h"
 #include "mla_internal.hpp"
@@ -736,6 +738,85 @@ mla_status mla_decode_attn_sparse(const mla_dims* dims, int32_t B, const void* q
     return fail(MLA_ERR_ALIGN, "decode_attn_sparse: indices and counts must be 4-byte aligned");
   return decode_attn_impl(dims, B, q, cache, counts, topk, num_splits, o_lat, lse, ws, ws_bytes, stream, indices,
                           topk);
+}
+
+mla_status mla_check_indices(const mla_dims* dims, int32_t B, const mla_cache* cache, const int32_t* pos,
+                             const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                             const int32_t* indices, int32_t topk, const int32_t* counts) {
+  MLA_TRY(check_dims(dims));
+  if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
+  MLA_TRY(check_cache(dims, cache));
+  const bool paged = cache->block_table != nullptr;
+  if (paged && !block_table && (pos || seq_lens || indices))
+    return fail(MLA_ERR_NULL, "check_indices: a paged cache needs the host copy of its block table");
+  if ((indices == nullptr) != (counts == nullptr))
+    return fail(MLA_ERR_NULL, "check_indices: indices and counts go together");
+  if (indices && topk <= 0) return fail(MLA_ERR_SHAPE, "check_indices: topk must be positive");
+  const long long bs = paged ? cache->block_size : 0;
+  const long long rows_max = paged ? static_cast<long long>(cache->max_blocks) * bs : cache->capacity;
+  // Block entry of row u of sequence b (paged): -1 when the entry is outside the pool.
+  auto block_of = [&](int b, long long u) -> long long {
+    const long long e = block_table[static_cast<long long>(b) * cache->max_blocks + u / bs];
+    return (e >= 0 && e < cache->n_blocks) ? e : -1;
+  };
+  if (pos) {
+    for (int b = 0; b < B; ++b) {
+      const long long t = pos[b];
+      if (t < 0 || t >= rows_max)
+        return fail(MLA_ERR_SHAPE, "check_indices: pos[%d] = %lld outside the sequence's %lld rows", b, t, rows_max);
+      if (paged && block_of(b, t) < 0)
+        return fail(MLA_ERR_SHAPE, "check_indices: pos[%d] = %lld falls in block-table entry %lld, not a block of "
+                    "the pool", b, t, t / bs);
+    }
+    if (paged) {
+      // two sequences appending into one cache slot would race
+      std::vector<long long> slots(B);
+      for (int b = 0; b < B; ++b) slots[b] = block_of(b, pos[b]) * bs + pos[b] % bs;
+      std::vector<long long> sorted(slots);
+      std::sort(sorted.begin(), sorted.end());
+      for (int i = 1; i < B; ++i)
+        if (sorted[i] == sorted[i - 1]) {
+          int b0 = -1, b1 = -1;
+          for (int b = 0; b < B; ++b)
+            if (slots[b] == sorted[i]) (b0 < 0 ? b0 : b1) = b;
+          return fail(MLA_ERR_SHAPE, "check_indices: sequences %d and %d append into the same cache slot", b0, b1);
+        }
+    }
+  }
+  if (seq_lens) {
+    if (max_seq_len < 0) return fail(MLA_ERR_SHAPE, "check_indices: negative max_seq_len");
+    for (int b = 0; b < B; ++b) {
+      const long long L = seq_lens[b];
+      if (L < 0 || L > max_seq_len)
+        return fail(MLA_ERR_SHAPE, "check_indices: seq_lens[%d] = %lld outside [0, max_seq_len = %d]", b, L,
+                    max_seq_len);
+      if (L > rows_max)
+        return fail(MLA_ERR_SHAPE, "check_indices: seq_lens[%d] = %lld exceeds the sequence's %lld rows", b, L,
+                    rows_max);
+      if (paged)
+        for (long long u = 0; u < L; u += bs)
+          if (block_of(b, u) < 0)
+            return fail(MLA_ERR_SHAPE, "check_indices: sequence %d reads rows of block-table entry %lld, not a "
+                        "block of the pool", b, u / bs);
+    }
+  }
+  if (indices) {
+    for (int b = 0; b < B; ++b) {
+      const long long n = counts[b];
+      if (n < 0 || n > topk)
+        return fail(MLA_ERR_SHAPE, "check_indices: counts[%d] = %lld outside [0, topk = %d]", b, n, topk);
+      const long long lim = seq_lens ? std::min<long long>(seq_lens[b], rows_max) : rows_max;
+      for (long long j = 0; j < n; ++j) {
+        const long long u = indices[static_cast<long long>(b) * topk + j];
+        if (u < 0 || u >= lim)
+          return fail(MLA_ERR_SHAPE, "check_indices: indices[%d][%lld] = %lld outside [0, %lld)", b, j, u, lim);
+        if (paged && block_of(b, u) < 0)
+          return fail(MLA_ERR_SHAPE, "check_indices: indices[%d][%lld] = %lld falls in block-table entry %lld, not "
+                      "a block of the pool", b, j, u, u / bs);
+      }
+    }
+  }
+  return ok();
 }
 
 mla_status mla_precompose(const mla_dims* dims, const void* W_UQ, const void* W_UK, const void* W_UV,

@@ -73,6 +73,9 @@ _SIGS = {
                                                ctypes.c_int32]),
     "mla_cache_row_bytes": (ctypes.c_size_t, [ctypes.POINTER(MLADims)]),
     "mla_decode_kernel": (ctypes.c_int32, [ctypes.POINTER(MLADims)]),
+    "mla_check_indices": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.POINTER(MLACache)]
+                          + [ctypes.c_void_p] * 2 + [ctypes.c_int32] + [ctypes.c_void_p] * 2 + [ctypes.c_int32]
+                          + [ctypes.c_void_p]),
     "mla_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -152,6 +155,32 @@ def cache_row_bytes(dims: MLADims) -> int:
 
 def decode_kernel(dims: MLADims) -> int:
     return lib().mla_decode_kernel(ctypes.byref(dims))
+
+
+def _host_i32(a, name):
+    """Host int32 array (numpy or CPU tensor) -> (keep-alive object, pointer)."""
+    if a is None:
+        return None, None
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError(f"{name} must be a host array (copy it back first)")
+        a = a.numpy()
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data
+
+
+def mla_check_indices(dims, B: int, cache: MLACache, pos=None, seq_lens=None, max_seq_len: int = 0,
+                      block_table=None, indices=None, counts=None) -> None:
+    """Check host copies of the positions, lengths, block table and top-k lists
+    the kernels read unchecked (see mla_check_indices in mla.h); raises
+    RuntimeError naming the first violation."""
+    keep = [_host_i32(a, n) for a, n in ((pos, "pos"), (seq_lens, "seq_lens"), (block_table, "block_table"),
+                                          (indices, "indices"), (counts, "counts"))]
+    topk = 0 if indices is None else int(keep[3][0].shape[-1])
+    _check(lib().mla_check_indices(ctypes.byref(dims), int(B), ctypes.byref(cache), keep[0][1], keep[1][1],
+                                   int(max_seq_len), keep[2][1], keep[3][1], topk, keep[4][1]),
+           "mla_check_indices")
 
 
 def mla_compress_append(dims, h_t, W_DKV, W_KR, gamma_kv, pos, cache: MLACache, ws, stream=None):

@@ -207,3 +207,93 @@ def test_prefill_auto_choice(L):
         pick = choose(4, T)
         assert L.mla_prefill_workspace_bytes(ctypes.byref(d), 4, T, 4096, ctypes.byref(c), AUTO) == \
             L.mla_prefill_workspace_bytes(ctypes.byref(d), 4, T, 4096, ctypes.byref(c), pick)
+
+
+# --------------------------------------------------------------------------
+# Host-side check of the device-side preconditions (mla_check_indices)
+# --------------------------------------------------------------------------
+
+def _expect(fn, code, text=None):
+    """Run a binding call; code 0 means it must pass, else it must raise with
+    that status (and mention text in the detail)."""
+    if code == OK:
+        fn()
+        return
+    with pytest.raises(RuntimeError) as e:
+        fn()
+    msg = str(e.value)
+    assert mla.lib().mla_status_str(code).decode() in msg, msg
+    if text:
+        assert text in msg, msg
+
+
+def test_check_indices_contiguous():
+    import numpy as np
+    d = v3()
+    c = mla.MLACache(A, None, 100, 0, 0, 0)
+    chk = lambda **kw: (lambda: mla.mla_check_indices(d, 3, c, **kw))
+    _expect(chk(pos=np.array([0, 50, 99])), OK)
+    _expect(chk(pos=np.array([0, 100, 5])), SHAPE, "pos[1] = 100")
+    _expect(chk(pos=np.array([-1, 1, 5])), SHAPE, "pos[0]")
+    _expect(chk(seq_lens=np.array([0, 100, 7]), max_seq_len=100), OK)
+    _expect(chk(seq_lens=np.array([0, 100, 7]), max_seq_len=99), SHAPE, "seq_lens[1]")
+    _expect(chk(seq_lens=np.array([0, 101, 7]), max_seq_len=101), SHAPE, "exceeds")
+    _expect(chk(seq_lens=np.array([0, -3, 7]), max_seq_len=10), SHAPE, "seq_lens[1]")
+    idx = np.array([[0, 5, 99], [3, 3, -1], [2, -1, -1]])
+    _expect(chk(indices=idx, counts=np.array([3, 2, 1])), OK)
+    _expect(chk(indices=idx, counts=np.array([3, 3, 1])), SHAPE, "indices[1][2] = -1")
+    _expect(chk(indices=idx, counts=np.array([4, 2, 1])), SHAPE, "counts[0] = 4")
+    # with lengths, listed rows must be below them
+    _expect(chk(indices=idx, counts=np.array([3, 2, 1]), seq_lens=np.array([100, 4, 3]), max_seq_len=100), OK)
+    _expect(chk(indices=idx, counts=np.array([3, 2, 1]), seq_lens=np.array([99, 4, 3]), max_seq_len=100),
+            SHAPE, "indices[0][2] = 99")
+    _expect(chk(indices=idx), NULL)
+
+
+def test_check_indices_paged():
+    import numpy as np
+    d = v3()
+    c = mla.MLACache(A, A, 0, 16, 4, 6)         # 6 blocks of 16 rows, 4 table entries per sequence
+    table = np.array([[0, 1, -1, -1], [2, 5, 3, -1]])
+    chk = lambda **kw: (lambda: mla.mla_check_indices(d, 2, c, block_table=table, **kw))
+    _expect(chk(pos=np.array([31, 47]), seq_lens=np.array([32, 48]), max_seq_len=48), OK)
+    _expect(chk(pos=np.array([32, 47])), SHAPE, "pos[0] = 32")                # entry 2 is -1
+    _expect(chk(pos=np.array([64, 0])), SHAPE, "pos[0] = 64")                 # past max_blocks * 16
+    _expect(chk(seq_lens=np.array([33, 48]), max_seq_len=48), SHAPE, "sequence 0")
+    _expect(chk(seq_lens=np.array([32, 49]), max_seq_len=64), SHAPE, "sequence 1")
+    bad = table.copy()
+    bad[1, 1] = 6                                                              # outside the pool of 6
+    _expect(lambda: mla.mla_check_indices(d, 2, c, block_table=bad, seq_lens=np.array([1, 20]), max_seq_len=20),
+            SHAPE, "entry 1")
+    # two sequences appending into one slot race
+    shared = np.array([[0, 1, -1, -1], [0, 5, 3, -1]])
+    _expect(lambda: mla.mla_check_indices(d, 2, c, block_table=shared, pos=np.array([3, 3])), SHAPE,
+            "same cache slot")
+    _expect(lambda: mla.mla_check_indices(d, 2, c, block_table=shared, pos=np.array([3, 4])), OK)
+    idx = np.array([[0, 31, 5], [47, 16, 0]])
+    _expect(chk(indices=idx, counts=np.array([3, 3])), OK)
+    _expect(chk(indices=np.array([[0, 32, 5], [1, 2, 3]]), counts=np.array([3, 3])), SHAPE, "indices[0][1] = 32")
+    # a paged check needs the host table
+    _expect(lambda: mla.mla_check_indices(d, 2, c, pos=np.array([1, 2])), NULL)
+    # nothing to check is fine; bad dims and caches are rejected as elsewhere
+    _expect(lambda: mla.mla_check_indices(d, 2, c), OK)
+    _expect(lambda: mla.mla_check_indices(d, 0, c), SHAPE)
+    _expect(lambda: mla.mla_check_indices(d, 2, mla.MLACache(A, A, 0, 48, 4, 6)), UNSUPPORTED)
+
+
+def test_check_indices_accepts_the_generated_workloads():
+    """The seeded workloads satisfy every precondition: the ragged paged batch
+    (shuffled table, -1 past each sequence) and the top-k lists."""
+    import numpy as np
+    from kv_cache_compression_mla_amd import inputs as gen
+    cfg = gen.CONFIGS["v3_b1_ctx4k"].with_(name="chk", B=5, ctx=None, ctx_range=(1, 300), paged=True,
+                                            block_size=64, seed=3)
+    inp = gen.make_inputs(cfg, with_weights=False)
+    d = v3()
+    c = mla.MLACache(A, A, 0, cfg.block_size, inp.block_table.shape[1], inp.cache.shape[0])
+    L = inp.seq_lens.astype(np.int32)
+    mla.mla_check_indices(d, cfg.B, c, pos=inp.ctx, seq_lens=L, max_seq_len=int(L.max()),
+                          block_table=inp.block_table)
+    lists, counts = gen.make_topk_indices(cfg, inp.seq_lens, 64)
+    mla.mla_check_indices(d, cfg.B, c, seq_lens=L, max_seq_len=int(L.max()), block_table=inp.block_table,
+                          indices=lists, counts=counts)
