@@ -27,10 +27,15 @@ def to_device(a: Optional[np.ndarray], dtype: str, device="cuda") -> Optional[to
 
 
 class DeviceStep:
-    def __init__(self, inp: MLAInputs, num_splits: int = 0, device="cuda", ws_splits=(), precomposed=False):
+    def __init__(self, inp: MLAInputs, num_splits: int = 0, device="cuda", ws_splits=(), precomposed=False,
+                 poison=False):
         """ws_splits: further split counts the workspace must also cover.
         precomposed: form W_QK and W_OV once here and run the query and output
-        sides as one product each (no per-head outputs then)."""
+        sides as one product each (no per-head outputs then).
+        poison: before every library call, fill the workspace with 0xFF bytes
+        (NaN as float32) and the call's outputs with NaN, so that an output
+        element or a partial result the call fails to write cannot pass on a
+        value left by an earlier call (the tests use this; timing does not)."""
         cfg = inp.cfg
         self.cfg, self.inp, self.device = cfg, inp, device
         self.num_splits = num_splits
@@ -63,6 +68,7 @@ class DeviceStep:
         self.o_heads = torch.empty(B, H, cfg.d_v, dtype=tdt, device=device)
         self.out = torch.empty(B, cfg.d, dtype=tdt, device=device)
         self.precomposed = precomposed
+        self.poison = poison
         if precomposed:
             qin = cfg.d_cq if cfg.d_cq else cfg.d
             self.W_QK = torch.empty(H, cfg.d_c, qin, dtype=tdt, device=device)
@@ -75,11 +81,20 @@ class DeviceStep:
         n = self.cfg.topk if self.cfg.topk else self.max_seq_len
         return mla.decode_num_splits(self.dims, self.cfg.B, n, self.num_splits)
 
+    def _poison(self, *outs):
+        if self.poison:
+            self.ws.fill_(0xFF)
+            for t in outs:
+                if t is not None:
+                    t.fill_(float("nan"))
+
     def compress_append(self):
+        self._poison()
         mla.mla_compress_append(self.dims, self.h_t, self.W["W_DKV"], self.W["W_KR"],
                                 self.W.get("gamma_kv"), self.pos, self.cdesc, self.ws)
 
     def absorb_q(self):
+        self._poison(self.q)
         if self.precomposed:
             mla.mla_absorb_q_precomposed(self.dims, self.h_t, self.W["W_DQ"], self.W_QK, self.W["W_QR"],
                                          self.pos, self.q, self.ws)
@@ -89,6 +104,7 @@ class DeviceStep:
 
     def decode_attn(self, num_splits: Optional[int] = None):
         s = self.num_splits if num_splits is None else num_splits
+        self._poison(self.o_lat, self.lse)
         if self.cfg.topk:
             mla.mla_decode_attn_sparse(self.dims, self.q, self.cdesc, self.topk_idx, self.topk_counts,
                                        self.o_lat, self.lse, self.ws, s)
@@ -97,6 +113,7 @@ class DeviceStep:
                                 self.o_lat, self.lse, self.ws, s)
 
     def out_proj(self):
+        self._poison(self.o_heads, self.out)
         if self.precomposed:
             mla.mla_out_proj_precomposed(self.dims, self.o_lat, self.W_OV, self.out, self.ws)
             return
@@ -127,7 +144,9 @@ class DevicePrefill:
     ctx_b rows per sequence (the T tokens' own rows among them), q is the
     seeded per-head query [B][T][H][d_h + d_R]."""
 
-    def __init__(self, inp: MLAInputs, T: int, device="cuda", q_std: float = 1.0):
+    def __init__(self, inp: MLAInputs, T: int, device="cuda", q_std: float = 1.0, poison=False):
+        """poison: fill the workspace (0xFF bytes) and the outputs (NaN) before
+        every call, as DeviceStep does."""
         from .inputs import make_prefill_query
         cfg = inp.cfg
         self.cfg, self.inp, self.T = cfg, inp, T
@@ -151,7 +170,12 @@ class DevicePrefill:
         ws = max(mla.prefill_workspace_bytes(self.dims, cfg.B, T, self.max_seq_len, self.cdesc, a)
                  for a in (mla.PREFILL_MATERIALIZED, mla.PREFILL_ABSORBED))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.poison = poison
 
     def run(self, algo: int):
+        if self.poison:
+            self.ws.fill_(0xFF)
+            self.o.fill_(float("nan"))
+            self.lse.fill_(float("nan"))
         mla.mla_prefill_attn(self.dims, self.q, self.cdesc, self.seq_lens, self.max_seq_len, self.W_UK, self.W_UV,
                              algo, self.o, self.lse, self.ws)
