@@ -17,10 +17,10 @@ Two steps, each a plain command:
              factors the other calibration kernels give are recorded beside it.
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o p -- \\
-        python3 -m kv_cache_compression_mla_amd.hbm_traffic run
+        python3 hbm_traffic.py run
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT_W -o p -- \\
-        python3 -m kv_cache_compression_mla_amd.hbm_traffic run
-    python3 -m kv_cache_compression_mla_amd.hbm_traffic summarize OUT_F OUT_W \\
+        python3 hbm_traffic.py run
+    python3 hbm_traffic.py summarize OUT_F OUT_W \\
         profiles/attn_hbm_traffic_v3_b64_ctx8k.json
 """
 import argparse
@@ -31,7 +31,7 @@ import json
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SRC = os.path.join(ROOT, "kv_cache_compression_mla_amd", "csrc", "attn_mfma.hip")
 COPY_BYTES = 256 << 20
 KERNELS = {"attn": "attn_mfma_kernel", "combine": "combine_chunks", "copy": "MulFunctor",
@@ -111,10 +111,10 @@ def summarize(fetch_dir, write_dir, out_path, workload):
                            "raw_KiB_per_dispatch": {"FETCH_SIZE": f, "WRITE_SIZE": w}},
            "attn_source_sha256": sha,
            "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o p -- "
-                        f"python3 -m kv_cache_compression_mla_amd.hbm_traffic run --workload {workload}",
+                        f"python3 hbm_traffic.py run --workload {workload}",
                         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT_W -o p -- "
-                        f"python3 -m kv_cache_compression_mla_amd.hbm_traffic run --workload {workload}",
-                        "python3 -m kv_cache_compression_mla_amd.hbm_traffic summarize OUT_F OUT_W OUT.json"]}
+                        f"python3 hbm_traffic.py run --workload {workload}",
+                        "python3 hbm_traffic.py summarize OUT_F OUT_W OUT.json"]}
     with open(out_path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
