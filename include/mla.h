@@ -129,8 +129,13 @@ mla_status mla_compress_append(const mla_dims* dims, int32_t B, const void* h_t,
  *   q_R(i)   = RoPE(W_QR(i) c_Q, pos[b])  (same position as the key, [DONG] C2)
  *   q_lat(i) = W_UK(i)^T q_C(i)     (the key up-projection moved onto the
  *                                    query, [DONG] section 4)
- * Output q [B][H][d_c + d_R] in the storage dtype: q_lat followed by q_R,
- * the same width as a cache row so attention is one contraction over it.
+ * Output q [B][H][d_c + 2*d_R] in the storage dtype: q_lat, then q_R, then
+ * the low term of q_R (the storage-dtype nearest value of q_R minus its
+ * first term; zero for float32). The first d_c + d_R values have the width
+ * of a cache row, so attention is one contraction over it; the rotary part
+ * is carried as two terms because it dominates the scores at the
+ * DeepSeek-V3 widths and its rounding to bf16 alone would reach the softmax.
+ * c_Q and q_C stay float32 in the workspace for the same reason.
  */
 mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t,
                         const void* W_DQ, const void* W_UQ, const void* W_QR,
@@ -145,7 +150,9 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t,
  *   lse(i)   = ln sum_u exp(s(i,u))
  * ([CASS] "End-to-end flow": content and rotary dot products summed, softmax
  * over all history, weights applied to the cached latents.)
- *   q          [B][H][d_c + d_R] storage dtype (from mla_absorb_q)
+ *   q          [B][H][d_c + 2*d_R] storage dtype (from mla_absorb_q): per
+ *              head q_lat, q_R, low term of q_R; the score uses q_lat and
+ *              q_R + low term
  *   seq_lens   [B] int32 device: rows attended, the new token included; 0 gives
  *              an all-zero o_lat row and lse = -inf
  *   max_seq_len host upper bound of seq_lens (sizes the launch)
@@ -280,7 +287,7 @@ mla_status mla_precompose(const mla_dims* dims, const void* W_UQ, const void* W_
  *   c_Q      = W_DQ h_t[b]          (h_t[b] when d_cq == 0, W_DQ NULL)
  *   q_lat(i) = W_QK(i) c_Q
  *   q_R(i)   = RoPE(W_QR(i) c_Q, pos[b])
- * Output q [B][H][d_c + d_R] exactly as mla_absorb_q lays it out.
+ * Output q [B][H][d_c + 2*d_R] exactly as mla_absorb_q lays it out.
  * ws: mla_workspace_bytes(dims, B, ...) bytes suffice.
  */
 mla_status mla_absorb_q_precomposed(const mla_dims* dims, int32_t B, const void* h_t,

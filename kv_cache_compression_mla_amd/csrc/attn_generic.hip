@@ -59,9 +59,10 @@ __global__ __launch_bounds__(GT) void attn_generic_kernel(AttnArgs a) {
   const int s_idx = (blockIdx.x / a.H) % a.splits;
   const int b = blockIdx.x / (a.H * a.splits);
   const int tid = threadIdx.x;
-  const T* q = static_cast<const T*>(a.q) + (static_cast<long long>(b) * a.H + head) * D;
+  // query row [q_lat ; q_R ; low term of q_R]: the rotary part is the sum
+  const T* q = static_cast<const T*>(a.q) + (static_cast<long long>(b) * a.H + head) * (D + a.d_R);
   const T* cache = static_cast<const T*>(a.cache);
-  for (int k = tid; k < D; k += GT) qs[k] = Elem<T>::ld(q + k);
+  for (int k = tid; k < D; k += GT) qs[k] = Elem<T>::ld(q + k) + (k >= a.d_c ? Elem<T>::ld(q + k + a.d_R) : 0.f);
   const int L = virt_len(a.seq_lens, b, a.qpt);
   const int bc = a.qpt == 1 ? b : b / a.qpt;   // the cached sequence it reads
   const int r0 = s_idx * a.chunk;

@@ -7,6 +7,11 @@
 // up-projection moves onto the query; aicassindra MLA explainer, "End-to-end
 // flow": content and rotary dot products summed, softmax over all history).
 //
+// The rotary part of the query (q_R, which dominates the scores at the
+// DeepSeek-V3 widths) arrives as two bf16 terms, q_R = hi + lo, so that its
+// rounding does not reach the softmax; the score chain adds the low term
+// with four more MFMAs on the tile's rotary operands.
+//
 // Work decomposition: one workgroup = one sequence x one context chunk x all
 // H heads, four waves. The heads that share a latent row form two dense
 // contractions per 32-row tile:
@@ -61,6 +66,15 @@
 #include "mla_internal.hpp"
 
 namespace mla {
+#ifdef MLA_CLOCK_STAMPS
+// Measurement build only (libmla_stamps.so; the library itself is built
+// without it): every attention workgroup records the shader-clock counter
+// (s_memtime, which counts shader cycles) and the 100 MHz real-time counter
+// (s_memrealtime) at its start and at its end, so that clock_stamps.py can
+// report cycles per workgroup and the clock each ran at.
+constexpr int kStampSlots = 65536;
+__device__ unsigned long long g_clock_stamps[4 * kStampSlots];
+#endif
 namespace {
 
 constexpr int DC = 512;               // latent width
@@ -70,6 +84,12 @@ constexpr int TILE = 32;              // rows per stage
 constexpr int NTHREADS = 256;
 constexpr int DMA_PER_WAVE = 9;       // 8 latent rows + 1 rotary block per tile
 constexpr int QK_STEPS = DW / 16;     // 36 score MFMAs per tile
+// A query row is [q_lat (512) ; q_R (64) ; q_R's low term (64)]: the rotary
+// part dominates the scores at these widths, so it comes as two bf16 terms
+// (nearest value, nearest value of the remainder) and the score chain runs
+// four more MFMAs that reuse the tile's rotary operands for the low term.
+constexpr int QW = DW + 64;           // query row elements
+constexpr int QK_ALL = QK_STEPS + 4;  // score MFMAs per tile with the low term
 constexpr int QK_DIST = 4;            // score-operand reads in flight
 constexpr int PV_DIST = 3;            // value operands (pairs of reads) in flight
 // Fast pass: a head's reference maximum is its first tile's maximum. A later
@@ -474,6 +494,9 @@ void attn_mfma_kernel(Params p) {
   const int hq = w % NW;              // this wave's score head block
   const int qhead = 32 * hq + l32;    // this lane's score head
 
+#ifdef MLA_CLOCK_STAMPS
+  const unsigned long long stamp_t0 = __builtin_amdgcn_s_memtime(), stamp_r0 = __builtin_amdgcn_s_memrealtime();
+#endif
   const ChunkPlan plan = plan_chunks(p, reinterpret_cast<int*>(smem), reinterpret_cast<int*>(smem + LM_OFF));
   if (plan.b < 0) return;             // no chunk for this workgroup
   const int b = plan.b;
@@ -499,11 +522,11 @@ void attn_mfma_kernel(Params p) {
 
   // Query of this lane's head in MFMA B-operand order: step s, half h holds
   // columns 16s + 8h .. 16s + 8h + 7.
-  bf16x8 qreg[QK_STEPS];
+  bf16x8 qreg[QK_ALL];
   {
-    const uint16_t* qp = p.q + (static_cast<long long>(b) * p.H + qhead) * DW + 8 * h;
+    const uint16_t* qp = p.q + (static_cast<long long>(b) * p.H + qhead) * QW + 8 * h;
 #pragma unroll
-    for (int s = 0; s < QK_STEPS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    for (int s = 0; s < QK_ALL; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
   // O^T accumulators: block NW*c + hb holds columns of value block 4w + c
@@ -555,8 +578,10 @@ void attn_mfma_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < QK_DIST; ++i) a[i] = operand(i);
 #pragma unroll
-    for (int s = 0; s < QK_STEPS; ++s) {
+    for (int s = 0; s < QK_ALL; ++s) {
       const bf16x8 cur = a[s % QK_DIST];
+      // steps 36..39 (the rotary low term) reuse the rotary operands of steps
+      // 32..35, which stay in the ring: no refill past the last real step
       if (s + QK_DIST < QK_STEPS) a[s % QK_DIST] = operand(s + QK_DIST);
       if (s == 0)
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(cur), "v"(qreg[s]));
@@ -851,6 +876,15 @@ void attn_mfma_kernel(Params p) {
     }
     __syncthreads();
   }
+#ifdef MLA_CLOCK_STAMPS
+  if (tid == 0 && blockIdx.x < kStampSlots) {
+    unsigned long long* st = g_clock_stamps + 4 * blockIdx.x;
+    st[0] = stamp_t0;
+    st[1] = __builtin_amdgcn_s_memtime();
+    st[2] = stamp_r0;
+    st[3] = __builtin_amdgcn_s_memrealtime();
+  }
+#endif
 }
 
 // Exact merge of the chunk partials of one (b, head), for sequences with
@@ -962,3 +996,13 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace mla
+
+#ifdef MLA_CLOCK_STAMPS
+// Copy the stamps of workgroups 0..n-1 of the last attention launch ([n][4]:
+// start cycles, end cycles, start real time, end real time) to host memory.
+extern "C" int mla_clock_stamps(unsigned long long* host_dst, int n) {
+  if (n < 0 || n > mla::kStampSlots) return static_cast<int>(hipErrorInvalidValue);
+  return static_cast<int>(hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(mla::g_clock_stamps),
+                                              sizeof(unsigned long long) * 4 * n, 0, hipMemcpyDeviceToHost));
+}
+#endif

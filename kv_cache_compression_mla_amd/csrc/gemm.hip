@@ -40,10 +40,13 @@ struct GemmP {
   int out_bf16;
 };
 
+// fp32 activations (A_F32) enter the MFMA as two bf16 terms (split_bf16x2):
+// the tile holds both and each k step runs two MFMAs per block.
 template <int MT, bool A_F32, bool W_KN>
 __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
+  constexpr int AT = A_F32 ? 2 : 1;   // activation terms
   __shared__ __align__(16) u32x4 wt[2][GBN * 8];
-  __shared__ __align__(16) u32x4 at[2][32 * MT * 8];
+  __shared__ __align__(16) u32x4 at[2][AT][32 * MT * 8];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int n0 = blockIdx.x * GBN;
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
   const uint16_t* W = p.W + g * p.sWg;
 
   u32x4 wreg[4];
-  u32x4 areg[MT];
+  u32x4 areg[AT][MT];
 
   auto load_w = [&](int k0) {
 #pragma unroll
@@ -90,14 +93,20 @@ __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
           const float* A = static_cast<const float*>(p.A) + g * p.sAg + static_cast<long long>(m) * p.lda + k;
           const f32x4 x0 = *reinterpret_cast<const f32x4*>(A);
           const f32x4 x1 = *reinterpret_cast<const f32x4*>(A + 4);
-          areg[i] = u32x4{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
-                          pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+          uint32_t hi[4], lo[4];
+          split_bf16x2(x0[0], x0[1], &hi[0], &lo[0]);
+          split_bf16x2(x0[2], x0[3], &hi[1], &lo[1]);
+          split_bf16x2(x1[0], x1[1], &hi[2], &lo[2]);
+          split_bf16x2(x1[2], x1[3], &hi[3], &lo[3]);
+          areg[0][i] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+          areg[AT - 1][i] = u32x4{lo[0], lo[1], lo[2], lo[3]};
         } else {
           const uint16_t* A = static_cast<const uint16_t*>(p.A) + g * p.sAg + static_cast<long long>(m) * p.lda + k;
-          areg[i] = *reinterpret_cast<const u32x4*>(A);
+          areg[0][i] = *reinterpret_cast<const u32x4*>(A);
         }
       } else {
-        areg[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < AT; ++t) areg[t][i] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -120,7 +129,9 @@ __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < MT; ++i) at[buf][gslot((tid >> 3) + 32 * i, tid & 7)] = areg[i];
+    for (int t = 0; t < AT; ++t)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) at[buf][t][gslot((tid >> 3) + 32 * i, tid & 7)] = areg[t][i];
   };
 
   f32x16 acc[MT];
@@ -143,12 +154,14 @@ __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
       for (int j = 0; j < 4; ++j) {
         const u32x4 av = wt[buf][gslot(32 * w + l32, 2 * j + h)];
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const u32x4 bv = at[buf][gslot(32 * i + l32, 2 * j + h)];
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                           __builtin_bit_cast(bf16x8, bv), acc[i],
-                                                           0, 0, 0);
-        }
+        for (int t = 0; t < AT; ++t)
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const u32x4 bv = at[buf][t][gslot(32 * i + l32, 2 * j + h)];
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                             __builtin_bit_cast(bf16x8, bv), acc[i],
+                                                             0, 0, 0);
+          }
       }
       if (more) store_tiles(buf ^ 1);
       __syncthreads();
@@ -353,12 +366,20 @@ __global__ __launch_bounds__(GTH) void gemm_stream_kernel(GemmP p) {
           if constexpr (!A_F32) {
             av = *reinterpret_cast<const bf16x8*>(st + C::W_BYTES + 16 * (ra * 8 + (cw ^ ((ra >> 1) & 7))));
           } else {
+            // fp32 activations: two bf16 terms (split_bf16x2), two MFMAs
             const char* arow = st + C::W_BYTES + ra * 256;
             const int c0 = 2 * cw, c1 = 2 * cw + 1;
             const f32x4 x0 = *reinterpret_cast<const f32x4*>(arow + 16 * (c0 ^ (ra & 15)));
             const f32x4 x1 = *reinterpret_cast<const f32x4*>(arow + 16 * (c1 ^ (ra & 15)));
-            av = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
-                                                  pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])});
+            uint32_t hi[4], lo[4];
+            split_bf16x2(x0[0], x0[1], &hi[0], &lo[0]);
+            split_bf16x2(x0[2], x0[3], &hi[1], &lo[1]);
+            split_bf16x2(x1[0], x1[1], &hi[2], &lo[2]);
+            split_bf16x2(x1[2], x1[3], &hi[3], &lo[3]);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, wv), __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), acc[i],
+                0, 0, 0);
+            av = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
           }
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), av, acc[i], 0, 0, 0);
         }
@@ -591,7 +612,22 @@ __global__ void reduce_store_kernel(const float* __restrict__ P, int splits, int
   Elem<TO>::st(out + g * sOg + m * ldo + n, v);
 }
 
-// Rotary projection [M][G*d_R] -> rotated, stored at out[m*ldo + g*sOg + j].
+// A value stored as two terms of the storage type: the nearest value, then
+// the nearest value of the remainder (zero for float32).
+template <typename TO> struct TwoTerm;
+template <> struct TwoTerm<float> {
+  __device__ static __forceinline__ void st(float* hi, float* lo, float v) { *hi = v; *lo = 0.f; }
+};
+template <> struct TwoTerm<uint16_t> {
+  __device__ static __forceinline__ void st(uint16_t* hi, uint16_t* lo, float v) {
+    const uint16_t h = f32_to_bf16(v);
+    *hi = h;
+    *lo = f32_to_bf16(v - bf16_to_f32(h));
+  }
+};
+
+// Rotary projection [M][G*d_R] -> rotated, stored at out[m*ldo + g*sOg + j]
+// and, as its second term, at out[m*ldo + g*sOg + d_R + j].
 template <typename TO>
 __global__ __launch_bounds__(256) void reduce_rope_kernel(const float* __restrict__ P, int splits, int M, int G,
                                                           int d_R, const int32_t* __restrict__ pos, float theta,
@@ -634,8 +670,8 @@ __global__ __launch_bounds__(256) void reduce_rope_kernel(const float* __restric
       }
       const float c = cs[2 * jt], sn = cs[2 * jt + 1];
       TO* o = out + static_cast<long long>(m) * ldo + g * sOg + 2 * j;
-      Elem<TO>::st(o, x0 * c - x1 * sn);
-      Elem<TO>::st(o + 1, x0 * sn + x1 * c);
+      TwoTerm<TO>::st(o, o + d_R, x0 * c - x1 * sn);
+      TwoTerm<TO>::st(o + 1, o + d_R + 1, x0 * sn + x1 * c);
     }
     __syncthreads();   // the angles of the next row overwrite cs
   }
@@ -895,6 +931,35 @@ hipError_t launch_reduce_rope(const float* P, int splits, int M, int G, int d_R,
     reduce_rope_kernel<uint16_t><<<grid, 256, 0, stream>>>(P, splits, M, G, d_R, pos, theta, static_cast<uint16_t*>(out), ldo, sOg);
   else
     reduce_rope_kernel<float><<<grid, 256, 0, stream>>>(P, splits, M, G, d_R, pos, theta, static_cast<float*>(out), ldo, sOg);
+  return hipGetLastError();
+}
+
+// Rotary query of the prefill entries into the absorbed query rows: rows of
+// src [n][...] hold q_R at src + k*lds + off_src; dst rows get it at
+// dst + k*ldd + off_dst followed by a zero second term (the given q_R is
+// exact in the storage type).
+template <typename T>
+__global__ __launch_bounds__(256) void rope_query_copy_kernel(const T* __restrict__ src, long long lds, int off_src,
+                                                              T* __restrict__ dst, long long ldd, int off_dst,
+                                                              int d_R, long long n) {
+  const long long idx = blockIdx.x * 256LL + threadIdx.x;
+  if (idx >= n * d_R) return;
+  const long long k = idx / d_R;
+  const int j = static_cast<int>(idx % d_R);
+  T* o = dst + k * ldd + off_dst + j;
+  o[0] = src[k * lds + off_src + j];
+  o[d_R] = T(0);
+}
+
+hipError_t launch_rope_query_copy(const void* src, long long lds, int off_src, void* dst, long long ldd, int off_dst,
+                                  int d_R, long long n, int dtype, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n * d_R + 255) / 256));
+  if (dtype == MLA_BF16)
+    rope_query_copy_kernel<uint16_t><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(src), lds, off_src,
+                                                                static_cast<uint16_t*>(dst), ldd, off_dst, d_R, n);
+  else
+    rope_query_copy_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(src), lds, off_src,
+                                                             static_cast<float*>(dst), ldd, off_dst, d_R, n);
   return hipGetLastError();
 }
 

@@ -148,8 +148,10 @@ size_t ws_compress(const mla_dims* d, int B) {
                   align_up(part_bytes({B, d->d_c + d->d_R, d->d, 1}, d->dtype)));
 }
 
+// The query side keeps its intermediates c_Q and q_C in float32 (the GEMMs
+// read them as two bf16 terms), so their rounding does not reach the scores.
 size_t ws_absorb(const mla_dims* d, int B) {
-  const size_t es = elem_size(d->dtype);
+  const size_t es = sizeof(float);
   const int qin = d->d_cq ? d->d_cq : d->d;
   size_t p = 0;
   if (d->d_cq) p = part_bytes({B, d->d_cq, d->d, 1}, d->dtype);
@@ -179,7 +181,7 @@ size_t ws_attn(const mla_dims* d, int B, int max_seq_len, int num_splits) {
 // precomposed variant: c_Q, then partials of W_DQ, of the per-head W_QK
 // product and of W_QR; the output product over H*d_c inputs
 size_t ws_absorb_pre(const mla_dims* d, int B) {
-  const size_t es = elem_size(d->dtype);
+  const size_t es = sizeof(float);   // c_Q in float32, as in ws_absorb
   const int qin = d->d_cq ? d->d_cq : d->d;
   size_t p = 0;
   if (d->d_cq) p = part_bytes({B, d->d_cq, d->d, 1}, d->dtype);
@@ -213,18 +215,21 @@ mla_status gemm(const void* A, long long lda, long long sAg, bool a_f32, const v
 
 // Product stored to out[g*sOg + m*ldo + n] in dtype: directly by the GEMM when
 // it runs as one split, else through fp32 partials P and the reduce epilogue.
+// out_dtype: element type of out (MLA_FP32 or MLA_BF16); -1 = the storage dtype.
 mla_status gemm_store(const void* A, long long lda, long long sAg, bool a_f32, const void* W, long long ldw,
                       long long sWg, bool w_kn, const GemmShape& s, int dtype, float* P, void* out,
-                      long long ldo, long long sOg, hipStream_t st) {
+                      long long ldo, long long sOg, hipStream_t st, int out_dtype = -1) {
+  if (out_dtype < 0) out_dtype = dtype;
   mla::GemmArgs g{A, lda, sAg, a_f32, W, ldw, sWg, w_kn, s.M, s.N, s.K, s.G, splits_for(s, dtype), P, dtype};
   g.out = out;
   g.ldo = ldo;
   g.sOg = sOg;
-  g.out_dtype = dtype;
+  g.out_dtype = out_dtype;
   if (mla::gemm_direct(g)) return hip_status(mla::launch_gemm(g, st), "gemm launch");
   g.out = nullptr;
   MLA_TRY(hip_status(mla::launch_gemm(g, st), "gemm launch"));
-  return hip_status(mla::launch_reduce_store(P, g.splits, s.G, s.M, s.N, out, ldo, sOg, dtype, st), "reduce launch");
+  return hip_status(mla::launch_reduce_store(P, g.splits, s.G, s.M, s.N, out, ldo, sOg, out_dtype, st),
+                    "reduce launch");
 }
 
 }  // namespace
@@ -343,39 +348,44 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const 
   const size_t es = elem_size(dt);
   const bool f32 = dt == MLA_FP32;
   const int H = dims->H, d_h = dims->d_h, d_R = dims->d_R, d_c = dims->d_c, D = d_c + d_R;
+  const int QD = D + d_R;   // query row: [q_lat ; q_R ; the low term of q_R]
+  // c_Q and q_C stay in float32 (the products read them as two bf16 terms)
   char* w = static_cast<char*>(ws);
   void* cq = w;
-  void* qC = w + align_up(static_cast<size_t>(B) * dims->d_cq * es);
-  float* P = reinterpret_cast<float*>(static_cast<char*>(qC) + align_up(static_cast<size_t>(B) * H * d_h * es));
+  void* qC = w + align_up(static_cast<size_t>(B) * dims->d_cq * sizeof(float));
+  float* P = reinterpret_cast<float*>(static_cast<char*>(qC) +
+                                      align_up(static_cast<size_t>(B) * H * d_h * sizeof(float)));
   // c_Q = W_DQ h (or h itself)
   const void* cin = h_t;
+  bool cin_f32 = f32;
   int qin = dims->d;
   if (dims->d_cq) {
     const GemmShape s{B, dims->d_cq, dims->d, 1};
-    MLA_TRY(gemm_store(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, cq, dims->d_cq, 0, st));
+    MLA_TRY(gemm_store(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, cq, dims->d_cq, 0, st, MLA_FP32));
     cin = cq;
+    cin_f32 = true;
     qin = dims->d_cq;
   }
   // q_C(i) = W_UQ(i) c_Q for all heads at once: W_UQ viewed as [H*d_h][qin]
   {
     const GemmShape s{B, H * d_h, qin, 1};
-    MLA_TRY(gemm_store(cin, qin, 0, f32, W_UQ, qin, 0, false, s, dt, P, qC, H * d_h, 0, st));
+    MLA_TRY(gemm_store(cin, qin, 0, cin_f32, W_UQ, qin, 0, false, s, dt, P, qC, H * d_h, 0, st, MLA_FP32));
   }
   // q_R(i) = RoPE(W_QR(i) c_Q, pos) into q[b][i][d_c:]
   {
     const GemmShape s{B, H * d_R, qin, 1};
-    MLA_TRY(gemm(cin, qin, 0, f32, W_QR, qin, 0, false, s, dt, P, st));
+    MLA_TRY(gemm(cin, qin, 0, cin_f32, W_QR, qin, 0, false, s, dt, P, st));
     void* qr = static_cast<char*>(q) + static_cast<size_t>(d_c) * es;
     MLA_TRY(hip_status(mla::launch_reduce_rope(P, splits_for(s, dt), B, H, d_R, pos, dims->rope_theta, qr,
-                                               static_cast<long long>(H) * D, D, dt, st),
+                                               static_cast<long long>(H) * QD, QD, dt, st),
                        "rope launch"));
   }
   // q_lat(i) = W_UK(i)^T q_C(i): per head g, A_g[b][k] = qC[b][g*d_h + k],
   // W_g(n=c, k) = W_UK[g][k][c] (k-major use of the [d_h][d_c] matrix).
   {
     const GemmShape s{B, d_c, d_h, H};
-    MLA_TRY(gemm_store(qC, static_cast<long long>(H) * d_h, d_h, f32, W_UK, d_c, static_cast<long long>(d_h) * d_c,
-                       true, s, dt, P, q, static_cast<long long>(H) * D, D, st));
+    MLA_TRY(gemm_store(qC, static_cast<long long>(H) * d_h, d_h, true, W_UK, d_c, static_cast<long long>(d_h) * d_c,
+                       true, s, dt, P, q, static_cast<long long>(H) * QD, QD, st));
   }
   return ok();
 }
@@ -521,7 +531,7 @@ PrefillPlan prefill_plan(const mla_dims* d, int B, int T, int max_seq_len, const
                                            paged ? 0 : static_cast<long long>(c->capacity) * D, false));
   } else {
     const long long BT = static_cast<long long>(B) * T;
-    pl.qa_bytes = static_cast<size_t>(BT) * H * D * es;
+    pl.qa_bytes = static_cast<size_t>(BT) * H * (D + d->d_R) * es;   // [q_lat ; q_R ; low term]
     pl.olat_bytes = static_cast<size_t>(BT) * H * d->d_c * sizeof(float);
     pl.attn_bytes = ws_attn(d, static_cast<int>(BT), max_seq_len, 0);
     const GemmShape sq{static_cast<int>(BT), d->d_c, d->d_h, H};
@@ -655,6 +665,7 @@ mla_status prefill_absorbed(const mla_dims* d, int B, int T, const void* q, cons
   const size_t es = elem_size(dt);
   const bool f32 = dt == MLA_FP32;
   const int H = d->H, D = d->d_c + d->d_R, DQ = d->d_h + d->d_R;
+  const int QD = D + d->d_R;   // absorbed query row: [q_lat ; q_R ; zero low term]
   const int BT = B * T;
   void* qa = w;
   w += align_up(pl.qa_bytes);
@@ -667,13 +678,11 @@ mla_status prefill_absorbed(const mla_dims* d, int B, int T, const void* q, cons
   {
     const GemmShape s{BT, d->d_c, d->d_h, H};
     MLA_TRY(gemm_store(q, static_cast<long long>(H) * DQ, DQ, f32, W_UK, d->d_c, static_cast<long long>(d->d_h) * d->d_c,
-                       true, s, dt, P, qa, static_cast<long long>(H) * D, D, st));
+                       true, s, dt, P, qa, static_cast<long long>(H) * QD, QD, st));
   }
-  // q_R(t, i) beside it
-  MLA_TRY(hip_status(hipMemcpy2DAsync(static_cast<char*>(qa) + static_cast<size_t>(d->d_c) * es, D * es,
-                                      static_cast<const char*>(q) + static_cast<size_t>(d->d_h) * es, DQ * es,
-                                      static_cast<size_t>(d->d_R) * es, static_cast<size_t>(BT) * H,
-                                      hipMemcpyDeviceToDevice, st),
+  // q_R(t, i) beside it (given in the storage type: its second term is zero)
+  MLA_TRY(hip_status(mla::launch_rope_query_copy(q, DQ, d->d_h, qa, QD, d->d_c, d->d_R,
+                                                 static_cast<long long>(BT) * H, dt, st),
                      "rotary query copy"));
   // token t of sequence b attends rows 0 .. seq_lens[b] - T + t
   MLA_TRY(decode_attn_impl(d, BT, qa, c, seq_lens, max_seq_len, 0, olat, lse, aw, pl.attn_bytes, st, nullptr, 0, T));
@@ -865,30 +874,33 @@ mla_status mla_absorb_q_precomposed(const mla_dims* dims, int32_t B, const void*
   const size_t es = elem_size(dt);
   const bool f32 = dt == MLA_FP32;
   const int H = dims->H, d_R = dims->d_R, d_c = dims->d_c, D = d_c + d_R;
+  const int QD = D + d_R;   // query row: [q_lat ; q_R ; the low term of q_R]
   char* w = static_cast<char*>(ws);
-  void* cq = w;
-  float* P = reinterpret_cast<float*>(w + align_up(static_cast<size_t>(B) * dims->d_cq * es));
+  void* cq = w;   // float32, as in mla_absorb_q
+  float* P = reinterpret_cast<float*>(w + align_up(static_cast<size_t>(B) * dims->d_cq * sizeof(float)));
   const void* cin = h_t;
+  bool cin_f32 = f32;
   int qin = dims->d;
   if (dims->d_cq) {
     const GemmShape s{B, dims->d_cq, dims->d, 1};
-    MLA_TRY(gemm_store(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, cq, dims->d_cq, 0, st));
+    MLA_TRY(gemm_store(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, cq, dims->d_cq, 0, st, MLA_FP32));
     cin = cq;
+    cin_f32 = true;
     qin = dims->d_cq;
   }
   // q_lat(i) = W_QK(i) c_Q: one activation row per sequence shared by all heads
   {
     const GemmShape s{B, d_c, qin, H};
-    MLA_TRY(gemm_store(cin, qin, 0, f32, W_QK, qin, static_cast<long long>(d_c) * qin, false, s, dt, P, q,
-                       static_cast<long long>(H) * D, D, st));
+    MLA_TRY(gemm_store(cin, qin, 0, cin_f32, W_QK, qin, static_cast<long long>(d_c) * qin, false, s, dt, P, q,
+                       static_cast<long long>(H) * QD, QD, st));
   }
   // q_R(i) = RoPE(W_QR(i) c_Q, pos), as in mla_absorb_q
   {
     const GemmShape s{B, H * d_R, qin, 1};
-    MLA_TRY(gemm(cin, qin, 0, f32, W_QR, qin, 0, false, s, dt, P, st));
+    MLA_TRY(gemm(cin, qin, 0, cin_f32, W_QR, qin, 0, false, s, dt, P, st));
     void* qr = static_cast<char*>(q) + static_cast<size_t>(d_c) * es;
     MLA_TRY(hip_status(mla::launch_reduce_rope(P, splits_for(s, dt), B, H, d_R, pos, dims->rope_theta, qr,
-                                               static_cast<long long>(H) * D, D, dt, st),
+                                               static_cast<long long>(H) * QD, QD, dt, st),
                        "rope launch"));
   }
   return ok();

@@ -35,6 +35,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{a, b}), v2bf));
 }
 
+// An fp32 activation carried into a bf16 MFMA as two bf16 terms: hi = the
+// nearest bf16 of x, lo = the nearest bf16 of x - hi (exact in fp32). hi + lo
+// equals x to about 2^-17 relative, so a product summed over both terms
+// keeps the activation's fp32 precision (the weights are bf16 already). Used
+// for the intermediate activations of the query and output sides, whose
+// rounding to bf16 would otherwise feed every head's scores.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t* hi, uint32_t* lo) {
+  const uint32_t h = pack_bf16x2(a, b);
+  *hi = h;
+  *lo = pack_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static __forceinline__ float ld(const float* p) { return *p; }
@@ -107,7 +119,9 @@ hipError_t launch_reduce_store(const float* P, int splits, int G, int M, int N,
                                void* out, long long ldo, long long sOg, int out_dtype,
                                hipStream_t stream);
 // Sum splits of the rotary projection [M][G*d_R] (g = head), rotate each head's
-// d_R vector at pos[m], store to out[m*ldo + g*sOg + j].
+// d_R vector at pos[m], store to out[m*ldo + g*sOg + j] as two terms of the
+// storage type: the nearest value, and at j + d_R the nearest value of the
+// remainder.
 hipError_t launch_reduce_rope(const float* P, int splits, int M, int G, int d_R,
                               const int32_t* pos, float theta, void* out,
                               long long ldo, long long sOg, int out_dtype,
@@ -118,6 +132,12 @@ hipError_t launch_reduce_rope(const float* P, int splits, int M, int G, int d_R,
 hipError_t launch_append(const float* Pc, int splits_c, int ldc, const float* Pr, int splits_r, int ldr, int M,
                          int d_c, int d_R, const void* gamma, float eps, const int32_t* pos,
                          float theta, const mla_cache& cache, int dtype, hipStream_t stream);
+
+// Copy n rotary query vectors (d_R values at src + k*lds + off_src) into the
+// absorbed query rows at dst + k*ldd + off_dst, each followed by a zero
+// second term.
+hipError_t launch_rope_query_copy(const void* src, long long lds, int off_src, void* dst, long long ldd, int off_dst,
+                                  int d_R, long long n, int dtype, hipStream_t stream);
 
 // Offline composition C(g, m, n) = sum_k X(g, k, m) Y(g, k, n) with element
 // strides (see gemm.hip); fp32 accumulation, stored in dtype.

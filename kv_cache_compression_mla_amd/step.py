@@ -62,7 +62,8 @@ class DeviceStep:
         ws_bytes = max(mla.workspace_bytes(self.dims, B, max(self.max_seq_len, cfg.topk), s)
                        for s in (num_splits, *ws_splits))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
-        self.q = torch.empty(B, H, D, dtype=tdt, device=device)
+        # query rows [q_lat ; q_R ; low term of q_R]
+        self.q = torch.empty(B, H, D + cfg.d_R, dtype=tdt, device=device)
         self.o_lat = torch.empty(B, H, cfg.d_c, dtype=torch.float32, device=device)
         self.lse = torch.empty(B, H, dtype=torch.float32, device=device)
         self.o_heads = torch.empty(B, H, cfg.d_v, dtype=tdt, device=device)

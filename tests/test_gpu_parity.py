@@ -16,7 +16,7 @@ import torch
 
 from kv_cache_compression_mla_amd import inputs as gen
 from kv_cache_compression_mla_amd import mla
-from kv_cache_compression_mla_amd.step import DeviceStep
+from kv_cache_compression_mla_amd.step import DeviceStep, to_device
 from oracle import mla_oracle as om
 from _common import make_inputs
 
@@ -40,6 +40,14 @@ def rel_err(got, ref):
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), "non-finite output"
     return np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+
+
+def query_rows(q_bits, cfg):
+    """A generator-made query [B][H][d_c + d_R] as the attention call takes it:
+    [q_lat ; q_R ; low term of q_R], the low term zero (the given q_R is
+    exact in the storage dtype)."""
+    lo = np.zeros(q_bits.shape[:-1] + (cfg.d_R,), dtype=q_bits.dtype)
+    return to_device(np.concatenate([q_bits, lo], axis=-1), cfg.dtype)
 
 
 def weights64(inp):
@@ -81,7 +89,12 @@ def check_step(inp, st, seqs=None, unabsorbed=True, label=""):
         a = r["abs"]
         row = st.cache_row(b, int(inp.ctx[b]))
         e_row = rel_err(row, a["row"])
-        e_q = rel_err(q[b], a["q"])
+        # q rows: [q_lat ; q_R ; low term of q_R]; the first two against the
+        # bf16 bar, the rotary part's two terms together much closer
+        D, dc = cfg.D, cfg.d_c
+        e_q = rel_err(q[b][:, :D], a["q"])
+        e_qr = rel_err(q[b][:, dc:D] + q[b][:, D:], a["q"][:, dc:])
+        assert e_qr <= (1e-4 if cfg.dtype == "bf16" else 1e-6), (label, b, "q_R two terms", e_qr)
         e_olat = rel_err(o_lat[b], a["o_lat"])
         e_lse = np.abs(lse[b] - a["lse"]).max() / max(np.abs(a["lse"]).max(), 1.0)
         ref = r["unabs"] if unabsorbed else a
@@ -294,8 +307,7 @@ def fill_append_slots(inp):
 def attention_only(inp, q_bits, num_splits):
     """Run mla_decode_attn alone on a generator-made query."""
     st = DeviceStep(inp, poison=True, num_splits=num_splits)
-    from kv_cache_compression_mla_amd.step import to_device
-    q = to_device(q_bits, inp.cfg.dtype)
+    q = query_rows(q_bits, inp.cfg)
     st._poison(st.o_lat, st.lse)
     mla.mla_decode_attn(st.dims, q, st.cdesc, st.seq_lens, st.max_seq_len, st.o_lat, st.lse, st.ws,
                         num_splits)
@@ -362,7 +374,7 @@ def test_empty_sequences_in_a_batch():
         st = DeviceStep(inp, poison=True, num_splits=splits)
         st.seq_lens.copy_(torch.from_numpy(lens).to(st.seq_lens.device))
         st._poison(st.o_lat, st.lse)
-        mla.mla_decode_attn(st.dims, to_device(q, cfg.dtype), st.cdesc, st.seq_lens, int(lens.max()),
+        mla.mla_decode_attn(st.dims, query_rows(q, cfg), st.cdesc, st.seq_lens, int(lens.max()),
                             st.o_lat, st.lse, st.ws, splits)
         torch.cuda.synchronize()
         o_lat, lse = st.host(st.o_lat), st.host(st.lse)
@@ -387,7 +399,7 @@ def sparse_only(inp, q_bits, lists, counts, num_splits):
     from kv_cache_compression_mla_amd.step import to_device
     dev = st.seq_lens.device
     st._poison(st.o_lat, st.lse)
-    mla.mla_decode_attn_sparse(st.dims, to_device(q_bits, inp.cfg.dtype), st.cdesc,
+    mla.mla_decode_attn_sparse(st.dims, query_rows(q_bits, inp.cfg), st.cdesc,
                                torch.from_numpy(lists).to(dev), torch.from_numpy(counts).to(dev),
                                st.o_lat, st.lse, st.ws, num_splits)
     torch.cuda.synchronize()
@@ -467,7 +479,7 @@ def test_all_sequences_empty():
             st = DeviceStep(inp, poison=True, num_splits=splits)
             st.seq_lens.zero_()
             st._poison(st.o_lat, st.lse)
-            mla.mla_decode_attn(st.dims, to_device(q, cfg.dtype), st.cdesc, st.seq_lens, 0, st.o_lat, st.lse,
+            mla.mla_decode_attn(st.dims, query_rows(q, cfg), st.cdesc, st.seq_lens, 0, st.o_lat, st.lse,
                                 st.ws, splits)
             torch.cuda.synchronize()
             say(f"all empty {cfg.name} splits={splits}")
