@@ -9,7 +9,8 @@ synthetic tensors of the DeepSeek-V3 geometry, resident in HBM before timing.
 Headline: decode-attention TFLOP/s (algorithmic FLOPs 2*H*(D + d_c) per
 attended row) and latent-cache GB/s (1152 B per attended row) of the
 mla_decode_attn call, both from HIP events recorded on the stream the library
-launches on; ms_per_step is the whole step (wall clock over the K timed
+launches on (created with hipEventReleaseToDevice, the runtime's flag for
+timing the commands between events without a system-scope cache flush); ms_per_step is the whole step (wall clock over the K timed
 steps, whose only events are the two around the attention call) and calls_ms
 the mean time of each of the four calls from a separate untimed pass with
 events between them. The roofline object prices the
@@ -46,7 +47,7 @@ def attn_work(cfg, seq_lens):
     rows = int(seq_lens.sum())
     row_bytes = cfg.D * 2
     cache_bytes = rows * row_bytes
-    q_bytes = cfg.B * cfg.H * cfg.D * 2
+    q_bytes = cfg.B * cfg.H * (cfg.D + cfg.d_R) * 2     # [q_lat ; q_R ; low term of q_R]
     out_bytes = cfg.B * cfg.H * cfg.d_c * 4 + cfg.B * cfg.H * 4
     flops = rows * 2 * cfg.H * (cfg.D + cfg.d_c)
     return rows, cache_bytes, cache_bytes + q_bytes + out_bytes, flops
@@ -196,6 +197,55 @@ def prefill_sweep(Ts, steps, warmup):
         torch.cuda.empty_cache()
 
 
+class DeviceEvents:
+    """HIP events for timing the attention call on the library's stream,
+    created with hipEventReleaseToDevice: recording one performs a
+    device-scope release instead of the default system-scope one, which the
+    HIP runtime documents as the way to time the commands between events more
+    precisely (the default event writes back and invalidates caches for the
+    host, and that costs the kernels after it). The events come from the HIP
+    runtime torch itself loaded, so they share its streams."""
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self, torch):
+        import ctypes
+        self.ct = ctypes
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        if not os.path.exists(path):
+            path = "/opt/rocm/lib/libamdhip64.so"
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.RELEASE_TO_DEVICE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def measured_copy_gbps(torch, nbytes=1 << 30, reps=10):
     """Device-to-device copy rate of this GPU (bytes read + written per
     second), the practical counterpart of the published HBM peak."""
@@ -263,7 +313,8 @@ def main():
     # timed region: K whole steps; the only events in it are the two around
     # the attention call (each event is a marker packet that costs the
     # stream a few microseconds, so per-call events would inflate the step)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    dev_ev = DeviceEvents(torch)
+    ev = [(dev_ev.create(), dev_ev.create()) for _ in range(args.steps)]
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
@@ -272,32 +323,32 @@ def main():
     for k in range(args.steps):
         st.compress_append()
         st.absorb_q()
-        ev[k][0].record(stream)
+        dev_ev.record(ev[k][0], stream)
         st.decode_attn()
-        ev[k][1].record(stream)
+        dev_ev.record(ev[k][1], stream)
         st.out_proj()
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
-    attn_times = [a.elapsed_time(b) for a, b in ev]
+    attn_times = [dev_ev.elapsed_ms(a, b) for a, b in ev]
     attn_ms = float(np.mean(attn_times))
     ms_per_step = t_total * 1e3 / args.steps
 
     # per-call breakdown, after the timed region: events between all four calls
     calls = ("compress_append", "absorb_q", "decode_attn", "out_proj")
     nb = min(args.steps, 10)
-    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(nb)]
+    evc = [[dev_ev.create() for _ in range(len(calls) + 1)] for _ in range(nb)]
     for e in evc:
-        e[0].record(stream)
+        dev_ev.record(e[0], stream)
         st.compress_append()
-        e[1].record(stream)
+        dev_ev.record(e[1], stream)
         st.absorb_q()
-        e[2].record(stream)
+        dev_ev.record(e[2], stream)
         st.decode_attn()
-        e[3].record(stream)
+        dev_ev.record(e[3], stream)
         st.out_proj()
-        e[4].record(stream)
+        dev_ev.record(e[4], stream)
     torch.cuda.synchronize()
-    calls_ms = {c: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evc])), 5)
+    calls_ms = {c: round(float(np.mean([dev_ev.elapsed_ms(e[i], e[i + 1]) for e in evc])), 5)
                 for i, c in enumerate(calls)}
 
     copy_gbps = measured_copy_gbps(torch)
@@ -330,7 +381,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "mla_decode_attn call (attn_mfma_kernel + combine_chunks)",
+                     "kernel": "mla_decode_attn call (attn_mfma_kernel, the chunks merged in the kernel; "
+                               "combine_chunks after it when a sequence has more than 4 chunks)",
                      "measured_copy_GBps": round(copy_gbps, 1),
                      "frac_of_copy": round(achieved_gbps / copy_gbps, 4),
                      "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
