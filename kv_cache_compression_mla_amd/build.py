@@ -12,6 +12,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
+# measurement build: the same sources with per-workgroup clock stamps in the
+# attention kernel (clock_stamps.py beside bench.py reads them)
+LIB_STAMPS = os.path.join(PKG, "libmla_stamps.so")
 SOURCES = ["attn_mfma.hip", "attn_generic.hip", "attn_prefill.hip", "gemm.hip", "mla_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -24,14 +27,17 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    objdir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, stamps: bool = False) -> str:
+    """Build libmla.so (or, with stamps, the measurement build libmla_stamps.so)."""
+    objdir = os.path.join(PKG, "_build_stamps" if stamps else "_build")
     os.makedirs(objdir, exist_ok=True)
+    extra = ["-DMLA_CLOCK_STAMPS"] if stamps else []
+    target = LIB_STAMPS if stamps else LIB
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"]
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -41,14 +47,15 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = target + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(verbose=True, stamps=True))
