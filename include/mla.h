@@ -178,6 +178,29 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q,
                            void* stream);
 
 /*
+ * mla_decode_attn_noalloc -- mla_decode_attn for callers that cannot allocate
+ * device memory or hold a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same arguments, results
+ * and errors as mla_decode_attn, without ws / ws_bytes: the scratch space
+ * (chunk partials, chunk plan) is a fixed array of MLA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends.
+ * The call allocates nothing; its first call on a device looks the array's
+ * address up once (hipGetSymbolAddress).
+ * Limit: the attention's scratch for these sizes (the attention part of
+ * mla_workspace_bytes) must fit the array, else MLA_ERR_WORKSPACE. At the
+ * DeepSeek-V3 widths (128 heads) the automatic plan fits for up to 280
+ * sequences on a 256-CU device.
+ * All calls on one device share the array and it keeps the last call's
+ * contents (no call relies on them): calls that overlap on one device, from
+ * different streams or threads, race and must be serialised by the caller.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (72u << 20)
+mla_status mla_decode_attn_noalloc(const mla_dims* dims, int32_t B, const void* q,
+                                   const mla_cache* cache, const int32_t* seq_lens,
+                                   int32_t max_seq_len, int32_t num_splits, float* o_lat,
+                                   float* lse, void* stream);
+
+/*
  * mla_decode_attn_sparse -- every head attends against a given subset of the
  * latent cache: sequence b attends only to the counts[b] rows listed in
  * indices[b][0..counts[b]) (positions in its cache), the top-k pattern of a

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "mla.h"
@@ -956,3 +957,52 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t B, const float* o_lat, con
 }
 
 }  // extern "C"
+
+// ---- allocation-free decode attention ----
+//
+// Scratch for mla_decode_attn_noalloc: one fixed array per device, held by the
+// loaded code object until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the device
+// symbol): the first call on each device looks its device address up with
+// hipGetSymbolAddress, and every later use goes through that address.
+namespace {
+
+__device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up once per device).
+mla_status scratch_address(void** out) {
+  int dev = 0;
+  MLA_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    MLA_TRY(hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!ptr) return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" mla_status mla_decode_attn_noalloc(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
+                                              const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits,
+                                              float* o_lat, float* lse, void* stream) {
+  MLA_TRY(check_dims(dims));
+  if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
+  if (max_seq_len < 0 || num_splits < 0) return fail(MLA_ERR_SHAPE, "negative max_seq_len or num_splits");
+  const size_t need = ws_attn(dims, B, max_seq_len, num_splits);
+  if (need > MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE, "decode_attn_noalloc needs %zu bytes of scratch, above the %zu-byte static array "
+                "(fewer sequences or splits per call)", need, static_cast<size_t>(MLA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  MLA_TRY(scratch_address(&ws));
+  return decode_attn_impl(dims, B, q, cache, seq_lens, max_seq_len, num_splits, o_lat, lse, ws,
+                          MLA_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
+}

@@ -48,6 +48,9 @@ _SIGS = {
                                        ctypes.POINTER(MLACache), ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_decode_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.POINTER(MLACache), ctypes.c_void_p, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "mla_decode_attn_sparse": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.POINTER(MLACache), ctypes.c_void_p, ctypes.c_int32,
                                               ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -211,6 +214,17 @@ def mla_decode_attn(dims, q, cache: MLACache, seq_lens, max_seq_len: int, o_lat,
         ctypes.byref(dims), B, _ptr(q, dt, "q"), ctypes.byref(cache), _ptr(seq_lens, torch.int32, "seq_lens"),
         int(max_seq_len), int(num_splits), _ptr(o_lat, torch.float32, "o_lat"),
         _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"), wsz, _stream(stream)), "mla_decode_attn")
+
+
+def mla_decode_attn_noalloc(dims, q, cache: MLACache, seq_lens, max_seq_len: int, o_lat, lse=None,
+                            num_splits: int = 0, stream=None):
+    """mla_decode_attn with the library's static per-device scratch (no workspace)."""
+    dt = dims.torch_dtype
+    B = q.shape[0]
+    _check(lib().mla_decode_attn_noalloc(
+        ctypes.byref(dims), B, _ptr(q, dt, "q"), ctypes.byref(cache), _ptr(seq_lens, torch.int32, "seq_lens"),
+        int(max_seq_len), int(num_splits), _ptr(o_lat, torch.float32, "o_lat"),
+        _ptr(lse, torch.float32, "lse"), _stream(stream)), "mla_decode_attn_noalloc")
 
 
 def mla_decode_attn_sparse(dims, q, cache: MLACache, indices, counts, o_lat, lse=None, ws=None,

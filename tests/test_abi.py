@@ -297,3 +297,16 @@ def test_check_indices_accepts_the_generated_workloads():
     lists, counts = gen.make_topk_indices(cfg, inp.seq_lens, 64)
     mla.mla_check_indices(d, cfg.B, c, seq_lens=L, max_seq_len=int(L.max()), block_table=inp.block_table,
                           indices=lists, counts=counts)
+
+def test_noalloc_rejects_sizes_beyond_its_static_scratch(L):
+    """mla_decode_attn_noalloc checks the scratch its sizes need against the
+    fixed array before it touches the device (no GPU needed for the error)."""
+    d = v3()
+    c = mla.MLACache(A, None, 100, 0, 0, 0)
+    call = lambda B, splits=0, maxlen=100: L.mla_decode_attn_noalloc(ctypes.byref(d), B, A, ctypes.byref(c), A,
+                                                                      maxlen, splits, A, None, None)
+    assert call(4096) == WORKSPACE
+    assert "static array" in L.mla_last_error().decode()
+    assert call(64, splits=8, maxlen=8192) == WORKSPACE   # 512 chunk partials of 128 x 512 floats
+    assert call(0) == SHAPE
+    assert L.mla_decode_attn_noalloc(None, 4, A, ctypes.byref(c), A, 100, 0, A, None, None) == NULL
