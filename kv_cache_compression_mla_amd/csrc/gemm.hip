@@ -40,11 +40,15 @@ struct GemmP {
   int out_bf16;
 };
 
-// fp32 activations (A_F32) enter the MFMA as two bf16 terms (split_bf16x2):
-// the tile holds both and each k step runs two MFMAs per block.
-template <int MT, bool A_F32, bool W_KN>
+// Activation kinds (AK): the storage dtype (A_STORE), float32 rounded once to
+// bf16 (A_F32), or float32 as two bf16 terms (A_SPLIT, split_bf16x2): the
+// tile then holds both terms and each k step runs two MFMAs per block.
+constexpr int A_STORE = 0, A_F32_ONE = 1, A_SPLIT = 2;
+
+template <int MT, int AK, bool W_KN>
 __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
-  constexpr int AT = A_F32 ? 2 : 1;   // activation terms
+  constexpr bool A_F32 = AK != A_STORE;
+  constexpr int AT = AK == A_SPLIT ? 2 : 1;   // activation terms
   __shared__ __align__(16) u32x4 wt[2][GBN * 8];
   __shared__ __align__(16) u32x4 at[2][AT][32 * MT * 8];
   const int tid = threadIdx.x;
@@ -93,13 +97,18 @@ __global__ __launch_bounds__(GTH) void gemm_mfma_kernel(GemmP p) {
           const float* A = static_cast<const float*>(p.A) + g * p.sAg + static_cast<long long>(m) * p.lda + k;
           const f32x4 x0 = *reinterpret_cast<const f32x4*>(A);
           const f32x4 x1 = *reinterpret_cast<const f32x4*>(A + 4);
-          uint32_t hi[4], lo[4];
-          split_bf16x2(x0[0], x0[1], &hi[0], &lo[0]);
-          split_bf16x2(x0[2], x0[3], &hi[1], &lo[1]);
-          split_bf16x2(x1[0], x1[1], &hi[2], &lo[2]);
-          split_bf16x2(x1[2], x1[3], &hi[3], &lo[3]);
-          areg[0][i] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-          areg[AT - 1][i] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+          if constexpr (AK == A_SPLIT) {
+            uint32_t hi[4], lo[4];
+            split_bf16x2(x0[0], x0[1], &hi[0], &lo[0]);
+            split_bf16x2(x0[2], x0[3], &hi[1], &lo[1]);
+            split_bf16x2(x1[0], x1[1], &hi[2], &lo[2]);
+            split_bf16x2(x1[2], x1[3], &hi[3], &lo[3]);
+            areg[0][i] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            areg[AT - 1][i] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+          } else {
+            areg[0][i] = u32x4{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                               pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+          }
         } else {
           const uint16_t* A = static_cast<const uint16_t*>(p.A) + g * p.sAg + static_cast<long long>(m) * p.lda + k;
           areg[0][i] = *reinterpret_cast<const u32x4*>(A);
@@ -285,8 +294,9 @@ struct StreamCfg {
   static_assert((NS - 1) * PER_WAVE < 64, "copies in flight fit the vmcnt counter");
 };
 
-template <int NT, int MT, bool A_F32>
+template <int NT, int MT, int AK>
 __global__ __launch_bounds__(GTH) void gemm_stream_kernel(GemmP p) {
+  constexpr bool A_F32 = AK != A_STORE;
   using C = StreamCfg<NT, MT, A_F32>;
   __shared__ __align__(1024) char smem[C::NS * C::STAGE];
   const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
@@ -366,20 +376,25 @@ __global__ __launch_bounds__(GTH) void gemm_stream_kernel(GemmP p) {
           if constexpr (!A_F32) {
             av = *reinterpret_cast<const bf16x8*>(st + C::W_BYTES + 16 * (ra * 8 + (cw ^ ((ra >> 1) & 7))));
           } else {
-            // fp32 activations: two bf16 terms (split_bf16x2), two MFMAs
             const char* arow = st + C::W_BYTES + ra * 256;
             const int c0 = 2 * cw, c1 = 2 * cw + 1;
             const f32x4 x0 = *reinterpret_cast<const f32x4*>(arow + 16 * (c0 ^ (ra & 15)));
             const f32x4 x1 = *reinterpret_cast<const f32x4*>(arow + 16 * (c1 ^ (ra & 15)));
-            uint32_t hi[4], lo[4];
-            split_bf16x2(x0[0], x0[1], &hi[0], &lo[0]);
-            split_bf16x2(x0[2], x0[3], &hi[1], &lo[1]);
-            split_bf16x2(x1[0], x1[1], &hi[2], &lo[2]);
-            split_bf16x2(x1[2], x1[3], &hi[3], &lo[3]);
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, wv), __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), acc[i],
-                0, 0, 0);
-            av = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+            if constexpr (AK == A_F32_ONE) {
+              av = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                                                    pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])});
+            } else {
+              // two bf16 terms (split_bf16x2), two MFMAs
+              uint32_t hi[4], lo[4];
+              split_bf16x2(x0[0], x0[1], &hi[0], &lo[0]);
+              split_bf16x2(x0[2], x0[3], &hi[1], &lo[1]);
+              split_bf16x2(x1[0], x1[1], &hi[2], &lo[2]);
+              split_bf16x2(x1[2], x1[3], &hi[3], &lo[3]);
+              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, wv), __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}),
+                  acc[i], 0, 0, 0);
+              av = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+            }
           }
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), av, acc[i], 0, 0, 0);
         }
@@ -827,6 +842,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   // m blocks (of up to 128 rows) times k splits share the z grid dimension
   if (static_cast<long long>(a.splits) * ((a.M + 127) / 128) > 65535) return hipErrorInvalidValue;
   const int splits = a.splits;
+  const int ak = a.a_f32 ? (a.a_split ? A_SPLIT : A_F32_ONE) : A_STORE;
   const int ksteps = (a.K + GBK - 1) / GBK;
   const int kper = ((ksteps + splits - 1) / splits) * GBK;
   if (stream_ok(a)) {
@@ -843,8 +859,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     const int mblocks = (a.M + 32 * MT - 1) / (32 * MT);
     const dim3 grid((a.N + nt - 1) / nt, a.G, splits * mblocks);
 #define MLA_STREAM(NTV, MTV)                                                                     \
-  if (a.a_f32) gemm_stream_kernel<NTV, MTV, true><<<grid, GTH, 0, stream>>>(p);                  \
-  else gemm_stream_kernel<NTV, MTV, false><<<grid, GTH, 0, stream>>>(p);
+  if (ak == A_SPLIT) gemm_stream_kernel<NTV, MTV, A_SPLIT><<<grid, GTH, 0, stream>>>(p);         \
+  else if (ak == A_F32_ONE) gemm_stream_kernel<NTV, MTV, A_F32_ONE><<<grid, GTH, 0, stream>>>(p); \
+  else gemm_stream_kernel<NTV, MTV, A_STORE><<<grid, GTH, 0, stream>>>(p);
     if (nt == 128) {
       if (MT == 1) { MLA_STREAM(128, 1) } else if (MT == 2) { MLA_STREAM(128, 2) } else { MLA_STREAM(128, 4) }
     } else {
@@ -865,16 +882,16 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     const int MT = a.M <= 32 ? 1 : a.M <= 64 ? 2 : 4;
     const int mblocks = (a.M + 32 * MT - 1) / (32 * MT);
     const dim3 grid((a.N + GBN - 1) / GBN, a.G, splits * mblocks);
+#define MLA_GEMM_AK(MTV, AKV)                                                                    \
+  if (a.w_kn) gemm_mfma_kernel<MTV, AKV, true><<<grid, GTH, 0, stream>>>(p);                     \
+  else gemm_mfma_kernel<MTV, AKV, false><<<grid, GTH, 0, stream>>>(p);
 #define MLA_GEMM(MTV)                                                                            \
-  if (a.a_f32) {                                                                                 \
-    if (a.w_kn) gemm_mfma_kernel<MTV, true, true><<<grid, GTH, 0, stream>>>(p);                  \
-    else gemm_mfma_kernel<MTV, true, false><<<grid, GTH, 0, stream>>>(p);                        \
-  } else {                                                                                       \
-    if (a.w_kn) gemm_mfma_kernel<MTV, false, true><<<grid, GTH, 0, stream>>>(p);                 \
-    else gemm_mfma_kernel<MTV, false, false><<<grid, GTH, 0, stream>>>(p);                       \
-  }
+  if (ak == A_SPLIT) { MLA_GEMM_AK(MTV, A_SPLIT) }                                               \
+  else if (ak == A_F32_ONE) { MLA_GEMM_AK(MTV, A_F32_ONE) }                                      \
+  else { MLA_GEMM_AK(MTV, A_STORE) }
     if (MT == 1) { MLA_GEMM(1) } else if (MT == 2) { MLA_GEMM(2) } else { MLA_GEMM(4) }
 #undef MLA_GEMM
+#undef MLA_GEMM_AK
     return hipGetLastError();
   }
   const dim3 grid((a.N + 255) / 256, a.M, a.G * splits);

@@ -149,8 +149,8 @@ size_t ws_compress(const mla_dims* d, int B) {
                   align_up(part_bytes({B, d->d_c + d->d_R, d->d, 1}, d->dtype)));
 }
 
-// The query side keeps its intermediates c_Q and q_C in float32 (the GEMMs
-// read them as two bf16 terms), so their rounding does not reach the scores.
+// The query side keeps its intermediates c_Q and q_C in float32, so that the
+// products feeding the scores (W_QR, W_UK^T) can read them as two bf16 terms.
 size_t ws_absorb(const mla_dims* d, int B) {
   const size_t es = sizeof(float);
   const int qin = d->d_cq ? d->d_cq : d->d;
@@ -208,9 +208,13 @@ mla_status hip_status(hipError_t e, const char* what) {
     if (_s != MLA_OK) return _s;    \
   } while (0)
 
+// a_split: a float32 activation enters as two bf16 terms (about float32
+// precision for twice the MFMAs) instead of being rounded once to bf16.
 mla_status gemm(const void* A, long long lda, long long sAg, bool a_f32, const void* W, long long ldw,
-                long long sWg, bool w_kn, const GemmShape& s, int dtype, float* P, hipStream_t st) {
+                long long sWg, bool w_kn, const GemmShape& s, int dtype, float* P, hipStream_t st,
+                bool a_split = false) {
   mla::GemmArgs g{A, lda, sAg, a_f32, W, ldw, sWg, w_kn, s.M, s.N, s.K, s.G, splits_for(s, dtype), P, dtype};
+  g.a_split = a_split;
   return hip_status(mla::launch_gemm(g, st), "gemm launch");
 }
 
@@ -219,9 +223,10 @@ mla_status gemm(const void* A, long long lda, long long sAg, bool a_f32, const v
 // out_dtype: element type of out (MLA_FP32 or MLA_BF16); -1 = the storage dtype.
 mla_status gemm_store(const void* A, long long lda, long long sAg, bool a_f32, const void* W, long long ldw,
                       long long sWg, bool w_kn, const GemmShape& s, int dtype, float* P, void* out,
-                      long long ldo, long long sOg, hipStream_t st, int out_dtype = -1) {
+                      long long ldo, long long sOg, hipStream_t st, int out_dtype = -1, bool a_split = false) {
   if (out_dtype < 0) out_dtype = dtype;
   mla::GemmArgs g{A, lda, sAg, a_f32, W, ldw, sWg, w_kn, s.M, s.N, s.K, s.G, splits_for(s, dtype), P, dtype};
+  g.a_split = a_split;
   g.out = out;
   g.ldo = ldo;
   g.sOg = sOg;
@@ -350,7 +355,8 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const 
   const bool f32 = dt == MLA_FP32;
   const int H = dims->H, d_h = dims->d_h, d_R = dims->d_R, d_c = dims->d_c, D = d_c + d_R;
   const int QD = D + d_R;   // query row: [q_lat ; q_R ; the low term of q_R]
-  // c_Q and q_C stay in float32 (the products read them as two bf16 terms)
+  // c_Q and q_C stay in float32: W_QR (the rotary query, which dominates
+  // the scores) and W_UK^T read them as two bf16 terms, W_UQ rounds c_Q once
   char* w = static_cast<char*>(ws);
   void* cq = w;
   void* qC = w + align_up(static_cast<size_t>(B) * dims->d_cq * sizeof(float));
@@ -375,7 +381,7 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const 
   // q_R(i) = RoPE(W_QR(i) c_Q, pos) into q[b][i][d_c:]
   {
     const GemmShape s{B, H * d_R, qin, 1};
-    MLA_TRY(gemm(cin, qin, 0, cin_f32, W_QR, qin, 0, false, s, dt, P, st));
+    MLA_TRY(gemm(cin, qin, 0, cin_f32, W_QR, qin, 0, false, s, dt, P, st, /*a_split=*/true));
     void* qr = static_cast<char*>(q) + static_cast<size_t>(d_c) * es;
     MLA_TRY(hip_status(mla::launch_reduce_rope(P, splits_for(s, dt), B, H, d_R, pos, dims->rope_theta, qr,
                                                static_cast<long long>(H) * QD, QD, dt, st),
@@ -386,7 +392,7 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const 
   {
     const GemmShape s{B, d_c, d_h, H};
     MLA_TRY(gemm_store(qC, static_cast<long long>(H) * d_h, d_h, true, W_UK, d_c, static_cast<long long>(d_h) * d_c,
-                       true, s, dt, P, q, static_cast<long long>(H) * QD, QD, st));
+                       true, s, dt, P, q, static_cast<long long>(H) * QD, QD, st, -1, /*a_split=*/true));
   }
   return ok();
 }
@@ -898,7 +904,7 @@ mla_status mla_absorb_q_precomposed(const mla_dims* dims, int32_t B, const void*
   // q_R(i) = RoPE(W_QR(i) c_Q, pos), as in mla_absorb_q
   {
     const GemmShape s{B, H * d_R, qin, 1};
-    MLA_TRY(gemm(cin, qin, 0, cin_f32, W_QR, qin, 0, false, s, dt, P, st));
+    MLA_TRY(gemm(cin, qin, 0, cin_f32, W_QR, qin, 0, false, s, dt, P, st, /*a_split=*/true));
     void* qr = static_cast<char*>(q) + static_cast<size_t>(d_c) * es;
     MLA_TRY(hip_status(mla::launch_reduce_rope(P, splits_for(s, dt), B, H, d_R, pos, dims->rope_theta, qr,
                                                static_cast<long long>(H) * QD, QD, dt, st),

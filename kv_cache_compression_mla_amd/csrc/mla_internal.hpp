@@ -99,6 +99,9 @@ struct GemmArgs {
   // activation run as one launch.
   const void* W2 = nullptr;
   int n_split = 0;
+  // float32 activations (a_f32) as two bf16 terms (split_bf16x2): about
+  // float32 precision for twice the MFMAs; otherwise rounded once to bf16
+  bool a_split = false;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // True when launch_gemm stores a's product directly to a.out (one split on
