@@ -381,8 +381,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "mla_decode_attn call (attn_mfma_kernel, the chunks merged in the kernel; "
-                               "combine_chunks after it when a sequence has more than 4 chunks)",
+                     "kernel": "mla_decode_attn call (attn_mfma_kernel, then combine_chunks, which merges the "
+                               "chunks of every sequence cut into more than one)",
                      "measured_copy_GBps": round(copy_gbps, 1),
                      "frac_of_copy": round(achieved_gbps / copy_gbps, 4),
                      "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},

@@ -160,7 +160,7 @@ struct Params {
 //    Long and short sequences of a ragged batch thus finish together, and a
 //    batch of equal lengths gets ceil(L / C) chunks each.
 // A sequence of length 0 gets one empty chunk (output: zeros, lse -inf).
-constexpr int MIN_CHUNK = 256;
+constexpr int MIN_CHUNK = 128;
 struct ChunkPlan {
   int b, r0, r1;   // sequence and rows [r0, r1)
   int start, n;    // the sequence's chunks: [start, start + n)
@@ -836,6 +836,7 @@ void attn_mfma_kernel(Params p) {
   // contiguous run, 16 bytes per lane, so every store instruction writes
   // 1 KiB of consecutive output (16-byte pieces of 32 head rows per
   // instruction straight from the accumulators left HBM lines half written).
+  // The stores are nontemporal: nothing in this kernel reads them again.
   // D[i][head] of block (c, hb) holds column colbase(4w + c) + 32*((i&15)>>2)
   // + 4*(i>>4) + (i&3); register 4g + m of this lane is i = 8g + 4h + m.
   constexpr int OROW = 2 * 1024 + 16;   // staged row stride: rows 16 B apart on the banks
@@ -871,8 +872,8 @@ void attn_mfma_kernel(Params p) {
     float* dst = obase + 64LL * R * DC;
     for (int idx = tid; idx < nrows * (DC / 4); idx += NTHREADS) {
       const int row = idx >> 7, piece = idx & 127;
-      *reinterpret_cast<f32x4*>(dst + row * DC + 4 * piece) =
-          *reinterpret_cast<const f32x4*>(smem + row * OROW + 16 * piece);
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(smem + row * OROW + 16 * piece),
+                                  reinterpret_cast<f32x4*>(dst + row * DC + 4 * piece));
     }
     __syncthreads();
   }

@@ -627,6 +627,20 @@ __global__ void reduce_store_kernel(const float* __restrict__ P, int splits, int
   Elem<TO>::st(out + g * sOg + m * ldo + n, v);
 }
 
+// The same sum (G = 1) stored twice: in float32, and rounded once to bf16 for
+// the products that take the activation rounded (the rounding the streaming
+// GEMM applies to a float32 activation on load, so their results are the same).
+__global__ void reduce_store_dual_kernel(const float* __restrict__ P, int splits, int M, int N,
+                                         float* __restrict__ out32, uint16_t* __restrict__ out16) {
+  const long long idx = blockIdx.x * 256LL + threadIdx.x;
+  const long long total = static_cast<long long>(M) * N;
+  if (idx >= total) return;
+  float v = 0.f;
+  for (int s = 0; s < splits; ++s) v += P[s * total + idx];
+  out32[idx] = v;
+  out16[idx] = f32_to_bf16(v);
+}
+
 // A value stored as two terms of the storage type: the nearest value, then
 // the nearest value of the remainder (zero for float32).
 template <typename TO> struct TwoTerm;
@@ -935,6 +949,14 @@ hipError_t launch_reduce_store(const float* P, int splits, int G, int M, int N, 
     reduce_store_kernel<uint16_t><<<grid, 256, 0, stream>>>(P, splits, G, M, N, static_cast<uint16_t*>(out), ldo, sOg);
   else
     reduce_store_kernel<float><<<grid, 256, 0, stream>>>(P, splits, G, M, N, static_cast<float*>(out), ldo, sOg);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_store_dual(const float* P, int splits, int M, int N, float* out32, uint16_t* out16,
+                                    hipStream_t stream) {
+  const long long total = static_cast<long long>(M) * N;
+  reduce_store_dual_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), 256, 0, stream>>>(P, splits, M, N,
+                                                                                              out32, out16);
   return hipGetLastError();
 }
 

@@ -87,7 +87,7 @@ bool mfma_attn(const mla_dims* d) {
 // sequence (at most); balanced plan: one per compute unit, at least one per
 // sequence. The device cuts the sequences into chunks that fit this grid.
 constexpr int kMaxMfmaBatch = 32768;   // plan scratch: B ints of LDS
-constexpr int kMinChunk = 256;         // rows; the device plan's lower bound on the chunk size
+constexpr int kMinChunk = 128;         // rows; the device plan's lower bound on the chunk size
 int cdiv(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
 // explicit split count, clamped to the tiles of the longest sequence (more
 // would give the same chunks); 0 = balanced plan
@@ -150,7 +150,8 @@ size_t ws_compress(const mla_dims* d, int B) {
 }
 
 // The query side keeps its intermediates c_Q and q_C in float32, so that the
-// products feeding the scores (W_QR, W_UK^T) can read them as two bf16 terms.
+// products feeding the scores (W_QR, W_UK^T) can read them as two bf16 terms;
+// c_Q also in bf16 (bf16 storage), for W_UQ, which takes it rounded once.
 size_t ws_absorb(const mla_dims* d, int B) {
   const size_t es = sizeof(float);
   const int qin = d->d_cq ? d->d_cq : d->d;
@@ -159,8 +160,8 @@ size_t ws_absorb(const mla_dims* d, int B) {
   p = std::max(p, part_bytes({B, d->H * d->d_h, qin, 1}, d->dtype));
   p = std::max(p, part_bytes({B, d->H * d->d_R, qin, 1}, d->dtype));
   p = std::max(p, part_bytes({B, d->d_c, d->d_h, d->H}, d->dtype));
-  return align_up(static_cast<size_t>(B) * d->d_cq * es) + align_up(static_cast<size_t>(B) * d->H * d->d_h * es) +
-         align_up(p);
+  return align_up(static_cast<size_t>(B) * d->d_cq * es) + align_up(static_cast<size_t>(B) * d->d_cq * 2) +
+         align_up(static_cast<size_t>(B) * d->H * d->d_h * es) + align_up(p);
 }
 
 // MFMA path: partial (O, m, l) per chunk of the grid, then the plan's
@@ -188,7 +189,8 @@ size_t ws_absorb_pre(const mla_dims* d, int B) {
   if (d->d_cq) p = part_bytes({B, d->d_cq, d->d, 1}, d->dtype);
   p = std::max(p, part_bytes({B, d->d_c, qin, d->H}, d->dtype));
   p = std::max(p, part_bytes({B, d->H * d->d_R, qin, 1}, d->dtype));
-  return align_up(static_cast<size_t>(B) * d->d_cq * es) + align_up(p);
+  return align_up(static_cast<size_t>(B) * d->d_cq * es) + align_up(static_cast<size_t>(B) * d->d_cq * 2) +
+         align_up(p);
 }
 size_t ws_out_pre(const mla_dims* d, int B) { return align_up(part_bytes({B, d->d, d->H * d->d_c, 1}, d->dtype)); }
 
@@ -235,6 +237,17 @@ mla_status gemm_store(const void* A, long long lda, long long sAg, bool a_f32, c
   g.out = nullptr;
   MLA_TRY(hip_status(mla::launch_gemm(g, st), "gemm launch"));
   return hip_status(mla::launch_reduce_store(P, g.splits, s.G, s.M, s.N, out, ldo, sOg, out_dtype, st),
+                    "reduce launch");
+}
+
+// c_Q = W_DQ h in float32 and, with bf16 storage, a bf16 copy (the split
+// partials summed once into both).
+mla_status cq_product(const void* h_t, bool f32, const void* W_DQ, const GemmShape& s, int dt, float* P, void* cq,
+                      void* cq16, hipStream_t st) {
+  if (dt != MLA_BF16) return gemm_store(h_t, s.K, 0, f32, W_DQ, s.K, 0, false, s, dt, P, cq, s.N, 0, st, MLA_FP32);
+  MLA_TRY(gemm(h_t, s.K, 0, f32, W_DQ, s.K, 0, false, s, dt, P, st));
+  return hip_status(mla::launch_reduce_store_dual(P, splits_for(s, dt), s.M, s.N, static_cast<float*>(cq),
+                                                  static_cast<uint16_t*>(cq16), st),
                     "reduce launch");
 }
 
@@ -359,24 +372,29 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t, const 
   // the scores) and W_UK^T read them as two bf16 terms, W_UQ rounds c_Q once
   char* w = static_cast<char*>(ws);
   void* cq = w;
-  void* qC = w + align_up(static_cast<size_t>(B) * dims->d_cq * sizeof(float));
+  void* cq16 = w + align_up(static_cast<size_t>(B) * dims->d_cq * sizeof(float));
+  void* qC = static_cast<char*>(cq16) + align_up(static_cast<size_t>(B) * dims->d_cq * 2);
   float* P = reinterpret_cast<float*>(static_cast<char*>(qC) +
                                       align_up(static_cast<size_t>(B) * H * d_h * sizeof(float)));
   // c_Q = W_DQ h (or h itself)
   const void* cin = h_t;
   bool cin_f32 = f32;
+  const void* cin_uq = h_t;   // W_UQ's activation: c_Q rounded once (bf16 copy)
+  bool cin_uq_f32 = f32;
   int qin = dims->d;
   if (dims->d_cq) {
     const GemmShape s{B, dims->d_cq, dims->d, 1};
-    MLA_TRY(gemm_store(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, cq, dims->d_cq, 0, st, MLA_FP32));
+    MLA_TRY(cq_product(h_t, f32, W_DQ, s, dt, P, cq, cq16, st));
     cin = cq;
     cin_f32 = true;
+    cin_uq = f32 ? cq : cq16;
+    cin_uq_f32 = f32;
     qin = dims->d_cq;
   }
   // q_C(i) = W_UQ(i) c_Q for all heads at once: W_UQ viewed as [H*d_h][qin]
   {
     const GemmShape s{B, H * d_h, qin, 1};
-    MLA_TRY(gemm_store(cin, qin, 0, cin_f32, W_UQ, qin, 0, false, s, dt, P, qC, H * d_h, 0, st, MLA_FP32));
+    MLA_TRY(gemm_store(cin_uq, qin, 0, cin_uq_f32, W_UQ, qin, 0, false, s, dt, P, qC, H * d_h, 0, st, MLA_FP32));
   }
   // q_R(i) = RoPE(W_QR(i) c_Q, pos) into q[b][i][d_c:]
   {
@@ -883,22 +901,27 @@ mla_status mla_absorb_q_precomposed(const mla_dims* dims, int32_t B, const void*
   const int H = dims->H, d_R = dims->d_R, d_c = dims->d_c, D = d_c + d_R;
   const int QD = D + d_R;   // query row: [q_lat ; q_R ; the low term of q_R]
   char* w = static_cast<char*>(ws);
-  void* cq = w;   // float32, as in mla_absorb_q
-  float* P = reinterpret_cast<float*>(w + align_up(static_cast<size_t>(B) * dims->d_cq * sizeof(float)));
+  void* cq = w;   // float32 and a bf16 copy, as in mla_absorb_q
+  void* cq16 = w + align_up(static_cast<size_t>(B) * dims->d_cq * sizeof(float));
+  float* P = reinterpret_cast<float*>(static_cast<char*>(cq16) + align_up(static_cast<size_t>(B) * dims->d_cq * 2));
   const void* cin = h_t;
   bool cin_f32 = f32;
+  const void* cin_qk = h_t;   // W_QK's activation: c_Q rounded once
+  bool cin_qk_f32 = f32;
   int qin = dims->d;
   if (dims->d_cq) {
     const GemmShape s{B, dims->d_cq, dims->d, 1};
-    MLA_TRY(gemm_store(h_t, dims->d, 0, f32, W_DQ, dims->d, 0, false, s, dt, P, cq, dims->d_cq, 0, st, MLA_FP32));
+    MLA_TRY(cq_product(h_t, f32, W_DQ, s, dt, P, cq, cq16, st));
     cin = cq;
     cin_f32 = true;
+    cin_qk = f32 ? cq : cq16;
+    cin_qk_f32 = f32;
     qin = dims->d_cq;
   }
   // q_lat(i) = W_QK(i) c_Q: one activation row per sequence shared by all heads
   {
     const GemmShape s{B, d_c, qin, H};
-    MLA_TRY(gemm_store(cin, qin, 0, cin_f32, W_QK, qin, static_cast<long long>(d_c) * qin, false, s, dt, P, q,
+    MLA_TRY(gemm_store(cin_qk, qin, 0, cin_qk_f32, W_QK, qin, static_cast<long long>(d_c) * qin, false, s, dt, P, q,
                        static_cast<long long>(H) * QD, QD, st));
   }
   // q_R(i) = RoPE(W_QR(i) c_Q, pos), as in mla_absorb_q

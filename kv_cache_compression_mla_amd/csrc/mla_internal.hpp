@@ -121,6 +121,10 @@ int gemm_splits(int M, int N, int K, int G, int dtype);
 hipError_t launch_reduce_store(const float* P, int splits, int G, int M, int N,
                                void* out, long long ldo, long long sOg, int out_dtype,
                                hipStream_t stream);
+// Sum splits of an [M][N] product (G = 1, rows N apart) into out32 (float32)
+// and out16 (the same sums rounded to bf16).
+hipError_t launch_reduce_store_dual(const float* P, int splits, int M, int N, float* out32, uint16_t* out16,
+                                    hipStream_t stream);
 // Sum splits of the rotary projection [M][G*d_R] (g = head), rotate each head's
 // d_R vector at pos[m], store to out[m*ldo + g*sOg + j] as two terms of the
 // storage type: the nearest value, and at j + d_R the nearest value of the

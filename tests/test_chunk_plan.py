@@ -16,7 +16,7 @@ import pytest
 
 from kv_cache_compression_mla_amd import mla
 
-TILE, MIN_CHUNK, CUS = 32, 256, 256
+TILE, MIN_CHUNK, CUS = 32, 128, 256
 
 
 def seq_chunks(L, t):
@@ -90,9 +90,9 @@ def test_short_sequences_and_empty_ones():
 
 
 def test_min_chunk_bounds_partial_traffic():
-    # one sequence of 4097 rows: chunks of at least 256 rows
+    # one sequence of 4097 rows: chunks of at least 128 rows
     C, chunks = check([4097], 0, CUS)
-    assert C == MIN_CHUNK and len(chunks) == 17
+    assert C == MIN_CHUNK and len(chunks) == 33
 
 
 @pytest.mark.parametrize("B,L,splits", [(64, 8193, 0), (8, 32769, 0), (1, 4097, 0), (64, 8193, 4),
