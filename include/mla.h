@@ -188,7 +188,7 @@ mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q,
  * address up once (hipGetSymbolAddress).
  * Limit: the attention's scratch for these sizes (the attention part of
  * mla_workspace_bytes) must fit the array, else MLA_ERR_WORKSPACE. At the
- * DeepSeek-V3 widths (128 heads) the automatic plan fits for up to 280
+ * DeepSeek-V3 widths (128 heads) the automatic plan fits for up to 560
  * sequences on a 256-CU device.
  * All calls on one device share the array and it keeps the last call's
  * contents (no call relies on them): calls that overlap on one device, from

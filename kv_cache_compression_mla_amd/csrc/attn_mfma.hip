@@ -62,7 +62,10 @@
 //
 // Context splits: a workgroup covers rows [s*chunk, min((s+1)*chunk, L_b)).
 // With more than one split it writes unnormalised (O, m, l) partials, merged
-// exactly by attn_combine.
+// exactly by combine_chunks. O goes out in fp16 with a power-of-two scale
+// per (chunk, head): every element of the row is O * 2^-E with 2^E above the
+// row's largest magnitude, so no element overflows and each keeps 11 bits
+// relative to the row's maximum (half the bytes of float32 partials).
 #include "mla_internal.hpp"
 
 namespace mla {
@@ -122,6 +125,7 @@ __host__ __device__ constexpr bool per_row(int pm) { return pm == PAGED_SMALL ||
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -138,8 +142,8 @@ struct Params {
   float sl2;              // softmax scale * log2(e)
   float* o_lat;
   float* lse;
-  float* part_o;          // [grid][H][512] partials, by chunk
-  float* part_ml;         // [grid][H][2]
+  uint16_t* part_o;       // [grid][H][512] fp16 partials O * 2^-E, by chunk
+  float* part_ml;         // [grid][H][4]: m, l, E (the partial's scale exponent), unused
   int2* plan_seq;         // [B]: (first chunk, chunks) of each sequence
   const int32_t* indices; // gather modes: [B][topk] listed rows (seq_lens = counts)
   int topk;
@@ -466,6 +470,15 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+
+// Two floats -> packed fp16 pair (lo = a, hi = b), nearest-even.
+__device__ __forceinline__ uint32_t f16x2_bits(float a, float b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t u) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xffffu)));
 }
 
 // max / sum over both half-waves (lanes l and l ^ 32), VALU only
@@ -823,13 +836,17 @@ void attn_mfma_kernel(Params p) {
       if (p.lse) p.lse[b * p.H + qhead] = (m_ref + log2f(l_tot)) * 0.69314718055994531f;
     } else {
       const long long pidx = static_cast<long long>(gi) * p.H + qhead;
-      p.part_ml[pidx * 2] = m_ref;
-      p.part_ml[pidx * 2 + 1] = l_tot;
+      p.part_ml[pidx * 4] = m_ref;
+      p.part_ml[pidx * 4 + 1] = l_tot;
     }
   }
   __syncthreads();
-  // The accumulators are read next; cover the last MFMAs' latency.
+  // The accumulators are read next; cover the last MFMAs' latency. Each
+  // accumulator then passes through an empty asm, so that no copy of it (the
+  // compiler's own included) can be placed above the wait.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 4 * NW; ++i) asm volatile("" : "+a"(oacc[i]));
   // Epilogue through LDS (the tile stages are free now), 64 heads per
   // round: each wave writes its accumulator blocks of those heads into
   // head rows of 512 floats, then the workgroup stores the rows as one
@@ -839,19 +856,53 @@ void attn_mfma_kernel(Params p) {
   // The stores are nontemporal: nothing in this kernel reads them again.
   // D[i][head] of block (c, hb) holds column colbase(4w + c) + 32*((i&15)>>2)
   // + 4*(i>>4) + (i&3); register 4g + m of this lane is i = 8g + 4h + m.
-  constexpr int OROW = 2 * 1024 + 16;   // staged row stride: rows 16 B apart on the banks
-  static_assert(64 * OROW <= LM_OFF, "staged rows must not reach the per-head (m, l)");
-  float* obase = single ? p.o_lat + static_cast<long long>(b) * p.H * DC
-                        : p.part_o + static_cast<long long>(gi) * p.H * DC;
+  // A partial (more than one chunk) leaves as fp16 scaled by 2^-E per head
+  // row: a first pass over the accumulators records, per wave, the largest
+  // magnitude of its 128 columns of each head row (in the weight buffers,
+  // free now); the staging pass then takes E from the maximum of the four
+  // and writes the scaled values as fp16 rows.
+  constexpr int OROW = 2 * 1024 + 16;   // staged fp32 row stride: rows 16 B apart on the banks
+  constexpr int OROW16 = 1024 + 16;     // staged fp16 row stride
+  static_assert(64 * OROW <= ROPE_OFF, "staged rows must stay below the rotary slots and weight buffers");
+  float* hmax = reinterpret_cast<float*>(smem + P_OFF);   // [4 waves][64 rows]
 #pragma unroll
   for (int R = 0; R < (NW + 1) / 2; ++R) {
+    if (!single) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int hb = 2 * R + hh;
+        if (hb < NW) {
+          float amax = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float x;
+              asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(oacc[NW * c + hb][r]));
+              amax = max2(amax, __builtin_fabsf(x));
+            }
+          amax = max_halves(amax);
+          if (h == 0) hmax[64 * w + 32 * hh + l32] = amax;
+        }
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int hb = 2 * R + hh;
       if (hb < NW) {
         const int head = 32 * hb + l32;
-        const float inv = single ? 1.f / lm[2 * head + 1] : 1.f;
-        char* rowp = smem + (32 * hh + l32) * OROW;
+        float sc;
+        if (single) {
+          sc = 1.f / lm[2 * head + 1];
+        } else {
+          const int row = 32 * hh + l32;
+          const float mx = max2(max2(hmax[row], hmax[64 + row]), max2(hmax[128 + row], hmax[192 + row]));
+          int e;
+          (void)frexpf(mx, &e);   // mx < 2^e (e = 0 for a zero row)
+          sc = ldexpf(1.f, -e);
+          if (w == 0 && h == 0) p.part_ml[(static_cast<long long>(gi) * p.H + head) * 4 + 2] = static_cast<float>(e);
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           float x[16];
@@ -861,19 +912,33 @@ void attn_mfma_kernel(Params p) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int col = colbase(4 * w + c) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
-            *reinterpret_cast<f32x4*>(rowp + 4 * col) =
-                f32x4{x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv};
+            if (single) {
+              *reinterpret_cast<f32x4*>(smem + (32 * hh + l32) * OROW + 4 * col) =
+                  f32x4{x[4 * g] * sc, x[4 * g + 1] * sc, x[4 * g + 2] * sc, x[4 * g + 3] * sc};
+            } else {
+              *reinterpret_cast<u32x2*>(smem + (32 * hh + l32) * OROW16 + 2 * col) =
+                  u32x2{f16x2_bits(x[4 * g] * sc, x[4 * g + 1] * sc), f16x2_bits(x[4 * g + 2] * sc, x[4 * g + 3] * sc)};
+            }
           }
         }
       }
     }
     __syncthreads();
     const int nrows = min(64, p.H - 64 * R);
-    float* dst = obase + 64LL * R * DC;
-    for (int idx = tid; idx < nrows * (DC / 4); idx += NTHREADS) {
-      const int row = idx >> 7, piece = idx & 127;
-      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(smem + row * OROW + 16 * piece),
-                                  reinterpret_cast<f32x4*>(dst + row * DC + 4 * piece));
+    if (single) {
+      float* dst = p.o_lat + (static_cast<long long>(b) * p.H + 64 * R) * DC;
+      for (int idx = tid; idx < nrows * (DC / 4); idx += NTHREADS) {
+        const int row = idx >> 7, piece = idx & 127;
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(smem + row * OROW + 16 * piece),
+                                    reinterpret_cast<f32x4*>(dst + row * DC + 4 * piece));
+      }
+    } else {
+      uint16_t* dst = p.part_o + (static_cast<long long>(gi) * p.H + 64 * R) * DC;
+      for (int idx = tid; idx < nrows * (DC / 8); idx += NTHREADS) {
+        const int row = idx >> 6, piece = idx & 63;
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(smem + row * OROW16 + 16 * piece),
+                                    reinterpret_cast<f32x4*>(dst + row * DC + 8 * piece));
+      }
     }
     __syncthreads();
   }
@@ -890,7 +955,8 @@ void attn_mfma_kernel(Params p) {
 
 // Exact merge of the chunk partials of one (b, head), for sequences with
 // more than one chunk: M = max m_j, w_j = 2^(m_j - M),
-// o = sum_j w_j O_j / sum_j w_j l_j and lse = (M + log2 sum_j w_j l_j) ln 2.
+// o = sum_j w_j O_j / sum_j w_j l_j and lse = (M + log2 sum_j w_j l_j) ln 2,
+// with O_j = 2^E_j times its stored fp16 row.
 // Up to 64 chunks, lane j of each wave reads (m, l) of chunk j, so the
 // maximum, weights and denominator come from wave reductions; every thread
 // streams 4 columns of every partial once, groups of GRP loads issued before
@@ -904,24 +970,29 @@ __global__ __launch_bounds__(128) void combine_chunks(Params p) {
   if (n <= 1) return;
   const int lane = threadIdx.x & 63;
   constexpr int GRP = 4;
-  const long long so = static_cast<long long>(p.H) * DC;   // partial stride (floats)
-  const long long sm = 2LL * p.H;
-  const float* po = p.part_o + (static_cast<long long>(start) * p.H + head) * DC + 4 * threadIdx.x;
-  const float* pm = p.part_ml + (static_cast<long long>(start) * p.H + head) * 2;
-  auto load = [&](int j) { return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + j * so)); };
+  const long long so = static_cast<long long>(p.H) * DC;   // partial stride (elements)
+  const long long sm = 4LL * p.H;
+  const uint16_t* po = p.part_o + (static_cast<long long>(start) * p.H + head) * DC + 4 * threadIdx.x;
+  const float* pm = p.part_ml + (static_cast<long long>(start) * p.H + head) * 4;
+  auto load = [&](int j) {
+    const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(po + j * so));
+    return f32x4{f16_bits_to_f32(u[0]), f16_bits_to_f32(u[0] >> 16), f16_bits_to_f32(u[1]), f16_bits_to_f32(u[1] >> 16)};
+  };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, den = 0.f;
   if (n <= 64) {
     f32x4 v0 = load(0), v1 = load(1), v2 = load(min(2, n - 1)), v3 = load(min(3, n - 1));
     const float m = lane < n ? pm[lane * sm] : -INFINITY;
     const float l = lane < n ? pm[lane * sm + 1] : 0.f;
+    const int e = lane < n ? static_cast<int>(pm[lane * sm + 2]) : 0;
     M = m;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float w = lane < n ? exp2f(m - M) : 0.f;
-    den = w * l;
+    const float w0 = lane < n ? exp2f(m - M) : 0.f;
+    den = w0 * l;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+    const float w = ldexpf(w0, e);   // the weight of the stored (scaled) row
     for (int j = 0; j < n; j += GRP) {
       if (j > 0) {
         v0 = load(j);
@@ -939,7 +1010,7 @@ __global__ __launch_bounds__(128) void combine_chunks(Params p) {
     for (int j = 0; j < n; ++j) {
       const float w = exp2f(pm[j * sm] - M);
       den += w * pm[j * sm + 1];
-      acc += w * load(j);
+      acc += ldexpf(w, static_cast<int>(pm[j * sm + 2])) * load(j);
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -968,7 +1039,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
   p.sl2 = a.scale * 1.4426950408889634f;
   p.o_lat = a.o_lat;
   p.lse = a.lse;
-  p.part_o = a.part_o;
+  p.part_o = reinterpret_cast<uint16_t*>(a.part_o);   // fp16 partials on this path
   p.part_ml = a.part_ml;
   p.plan_seq = a.plan_seq;
   p.indices = a.indices;

@@ -164,11 +164,11 @@ size_t ws_absorb(const mla_dims* d, int B) {
          align_up(static_cast<size_t>(B) * d->H * d->d_h * es) + align_up(p);
 }
 
-// MFMA path: partial (O, m, l) per chunk of the grid, then the plan's
-// per-sequence (first chunk, chunks).
+// MFMA path: partial O (fp16, scaled) and (m, l, E) per chunk of the grid,
+// then the plan's per-sequence (first chunk, chunks).
 size_t ws_attn_mfma(const mla_dims* d, int B, int max_seq_len, int num_splits) {
   const size_t g = static_cast<size_t>(std::min(kMaxMfmaGrid, mfma_grid(B, mfma_splits(num_splits, max_seq_len))));
-  return align_up(g * d->H * d->d_c * sizeof(float)) + align_up(g * d->H * 2 * sizeof(float)) +
+  return align_up(g * d->H * d->d_c * 2) + align_up(g * d->H * 4 * sizeof(float)) +
          align_up(static_cast<size_t>(B) * 2 * sizeof(int));
 }
 size_t ws_attn(const mla_dims* d, int B, int max_seq_len, int num_splits) {
@@ -476,10 +476,10 @@ mla_status decode_attn_impl(const mla_dims* dims, int32_t B, const void* q, cons
     char* w = static_cast<char*>(ws);
     a.splits = s;
     a.grid = static_cast<int>(g);
-    a.part_o = reinterpret_cast<float*>(w);
-    w += align_up(g * dims->H * dims->d_c * sizeof(float));
+    a.part_o = reinterpret_cast<float*>(w);   // fp16 partials, read as such by the MFMA path
+    w += align_up(g * dims->H * dims->d_c * 2);
     a.part_ml = reinterpret_cast<float*>(w);
-    w += align_up(g * dims->H * 2 * sizeof(float));
+    w += align_up(g * dims->H * 4 * sizeof(float));
     a.plan_seq = reinterpret_cast<int2*>(w);
     MLA_TRY(hip_status(mla::launch_attn_mfma(a, st), "attention launch"));
     return ok();

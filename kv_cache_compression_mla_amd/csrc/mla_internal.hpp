@@ -165,8 +165,8 @@ struct AttnArgs {
   float scale;
   float* o_lat;
   float* lse;
-  float* part_o;    // generic: [B][splits][H][d_c]; MFMA: [grid][H][d_c], by chunk
-  float* part_ml;   // generic: [B][splits][H][2];   MFMA: [grid][H][2]
+  float* part_o;    // generic: [B][splits][H][d_c] fp32; MFMA: [grid][H][d_c] fp16 (scaled), by chunk
+  float* part_ml;   // generic: [B][splits][H][2];        MFMA: [grid][H][4] (m, l, E, unused)
   int dtype;
   // MFMA kernel: workgroups launched, and per sequence (first chunk, chunks)
   // of the plan it computes on the device (splits = 0: balanced plan)

@@ -68,7 +68,7 @@ def test_kernel_choice_and_split_plan():
     assert mla.decode_num_splits(tiny(), 1, 65, 0) >= 1
     assert mla.workspace_bytes(v3(), 64, 8193, 1) >= 256
     big = mla.workspace_bytes(v3(), 64, 8193, 4)
-    assert big >= 64 * 4 * 128 * 514 * 4
+    assert big >= 64 * 4 * 128 * (512 * 2 + 4 * 4)   # fp16 chunk partials and (m, l, E) per head
 
 
 def test_dims_validation(L):
@@ -307,6 +307,6 @@ def test_noalloc_rejects_sizes_beyond_its_static_scratch(L):
                                                                       maxlen, splits, A, None, None)
     assert call(4096) == WORKSPACE
     assert "static array" in L.mla_last_error().decode()
-    assert call(64, splits=8, maxlen=8192) == WORKSPACE   # 512 chunk partials of 128 x 512 floats
+    assert call(64, splits=16, maxlen=8192) == WORKSPACE   # 1024 chunk partials of 128 x 512 fp16 values
     assert call(0) == SHAPE
     assert L.mla_decode_attn_noalloc(None, 4, A, ctypes.byref(c), A, 100, 0, A, None, None) == NULL
