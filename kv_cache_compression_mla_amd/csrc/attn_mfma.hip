@@ -169,6 +169,7 @@ struct ChunkPlan {
   int b, r0, r1;   // sequence and rows [r0, r1)
   int start, n;    // the sequence's chunks: [start, start + n)
   int total;       // chunks in the plan (workgroups past it have no work)
+  int g;           // this workgroup's chunk (index of its partials)
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -189,6 +190,11 @@ __device__ __forceinline__ long long wave_sum64(long long v) {
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
   return v;
 }
 
@@ -248,7 +254,28 @@ __device__ ChunkPlan plan_chunks(const Params& p, int* scratch, int* res) {
     }
     const int total = __shfl(incl, 63);
     int start = incl - local;
-    const int g = blockIdx.x;
+    // Workgroup -> chunk. When every sequence has the same length (so the
+    // same chunk count n) and B is a multiple of 8, the n chunks of a
+    // sequence take workgroups 8 apart in launch order (groups of 8
+    // sequences x n chunks), which dispatch places on one XCD, so they read
+    // the sequence's query block through that XCD's L2. Otherwise
+    // workgroup x takes chunk x. Chunk indices stay in prefix order.
+    int lmin = 0x7fffffff, lmax = 0;
+    for (int i = lane; i < p.B; i += 64) {
+      lmin = min(lmin, scratch[i]);
+      lmax = max(lmax, scratch[i]);
+    }
+    lmin = wave_min(lmin);
+    lmax = wave_max(lmax);
+    int g = blockIdx.x;
+    if (lmin == lmax && (p.B & 7) == 0) {
+      int rows, n;
+      seq_chunks(lmax, p.splits > 0 ? p.splits : max(1, ceil_div(lmax, target_rows)), &rows, &n);
+      if (g < n * p.B) {
+        const int grp = g / (8 * n), r = g % (8 * n);
+        g = n * (8 * grp + (r & 7)) + (r >> 3);
+      }
+    }
     for (int i = lane * per; i < min(p.B, (lane + 1) * per); ++i) {
       const int L = scratch[i];
       int rows, n;
@@ -265,6 +292,7 @@ __device__ ChunkPlan plan_chunks(const Params& p, int* scratch, int* res) {
     }
     if (lane == 0) {
       res[5] = total;
+      res[6] = g;
       if (g >= total) res[0] = -1;
     }
   }
@@ -276,6 +304,7 @@ __device__ ChunkPlan plan_chunks(const Params& p, int* scratch, int* res) {
   c.start = __builtin_amdgcn_readfirstlane(res[3]);
   c.n = __builtin_amdgcn_readfirstlane(res[4]);
   c.total = __builtin_amdgcn_readfirstlane(res[5]);
+  c.g = __builtin_amdgcn_readfirstlane(res[6]);
   return c;
 }
 
@@ -514,7 +543,7 @@ void attn_mfma_kernel(Params p) {
   if (plan.b < 0) return;             // no chunk for this workgroup
   const int b = plan.b;
   const int bc = p.qpt == 1 ? b : b / p.qpt;   // the cached sequence it reads
-  const int gi = blockIdx.x;          // chunk index (partials)
+  const int gi = plan.g;              // chunk index (partials)
   const bool single = plan.n == 1;    // whole sequence here: final output
   if (tid == 0 && plan.r0 == 0) p.plan_seq[b] = int2{plan.start, plan.n};
   const int row_begin = plan.r0;

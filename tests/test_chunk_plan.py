@@ -103,3 +103,32 @@ def test_host_split_count_matches_the_plan(B, L, splits):
     grid = B * s if s else max(CUS, B)
     _, chunks = plan([L] * B, s, grid)
     assert mla.decode_num_splits(d, B, L, splits) == sum(1 for b, _, _ in chunks if b == 0)
+
+
+def workgroup_chunk(x, lens, n):
+    """The chunk workgroup x takes: with equal lengths (n chunks each) and B a
+    multiple of 8, chunks of a sequence sit 8 workgroups apart in groups of 8
+    sequences; otherwise workgroup x takes chunk x."""
+    B = len(lens)
+    if len(set(lens)) == 1 and B % 8 == 0 and x < n * B:
+        grp, r = divmod(x, 8 * n)
+        return n * (8 * grp + (r & 7)) + (r >> 3)
+    return x
+
+
+@pytest.mark.parametrize("B,L,splits", [(64, 8193, 0), (8, 32769, 0), (64, 2048, 0), (16, 100, 3), (24, 5000, 0)])
+def test_equal_lengths_put_a_sequences_chunks_on_one_xcd(B, L, splits):
+    grid = B * splits if splits else max(CUS, B)
+    _, chunks = check([L] * B, splits, grid)
+    n = len(chunks) // B
+    total = n * B
+    got = [workgroup_chunk(x, [L] * B, n) for x in range(total)]
+    assert sorted(got) == list(range(total))            # every chunk taken once
+    for b in range(B):
+        xs = [x for x in range(total) if got[x] // n == b]
+        assert len(xs) == n and len({x % 8 for x in xs}) == 1   # one XCD under round-robin dispatch
+
+
+def test_ragged_lengths_keep_the_identity_mapping():
+    lens = [100, 200] * 8
+    assert [workgroup_chunk(x, lens, 1) for x in range(16)] == list(range(16))
