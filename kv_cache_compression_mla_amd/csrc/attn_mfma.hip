@@ -66,6 +66,8 @@
 // per (chunk, head): every element of the row is O * 2^-E with 2^E above the
 // row's largest magnitude, so no element overflows and each keeps 11 bits
 // relative to the row's maximum (half the bytes of float32 partials).
+#include <type_traits>
+
 #include "mla_internal.hpp"
 
 namespace mla {
@@ -986,11 +988,11 @@ void attn_mfma_kernel(Params p) {
 // more than one chunk: M = max m_j, w_j = 2^(m_j - M),
 // o = sum_j w_j O_j / sum_j w_j l_j and lse = (M + log2 sum_j w_j l_j) ln 2,
 // with O_j = 2^E_j times its stored fp16 row.
-// Up to 64 chunks, lane j of each wave reads (m, l) of chunk j, so the
+// Up to 64 chunks, lane j of each wave reads (m, l, E) of chunk j, so the
 // maximum, weights and denominator come from wave reductions; every thread
-// streams 4 columns of every partial once, groups of GRP loads issued before
-// their weights are needed (padding loads re-read the last partial and weigh
-// 0). More chunks take a plain loop.
+// streams 4 columns of every partial once, in groups of 4 (up to four
+// chunks) or 16 loads issued before their weights are needed (padding loads
+// re-read the last partial and are not added). More chunks take a plain loop.
 __global__ __launch_bounds__(128) void combine_chunks(Params p) {
   const int head = blockIdx.x % p.H;
   const int b = blockIdx.x / p.H;
@@ -998,48 +1000,54 @@ __global__ __launch_bounds__(128) void combine_chunks(Params p) {
   const int start = pl.x, n = pl.y;
   if (n <= 1) return;
   const int lane = threadIdx.x & 63;
-  constexpr int GRP = 4;
   const long long so = static_cast<long long>(p.H) * DC;   // partial stride (elements)
   const long long sm = 4LL * p.H;
   const uint16_t* po = p.part_o + (static_cast<long long>(start) * p.H + head) * DC + 4 * threadIdx.x;
   const float* pm = p.part_ml + (static_cast<long long>(start) * p.H + head) * 4;
-  auto load = [&](int j) {
-    const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(po + j * so));
+  auto raw = [&](int j) { return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(po + j * so)); };
+  auto cvt = [](u32x2 u) {
     return f32x4{f16_bits_to_f32(u[0]), f16_bits_to_f32(u[0] >> 16), f16_bits_to_f32(u[1]), f16_bits_to_f32(u[1] >> 16)};
   };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, den = 0.f;
   if (n <= 64) {
-    f32x4 v0 = load(0), v1 = load(1), v2 = load(min(2, n - 1)), v3 = load(min(3, n - 1));
-    const float m = lane < n ? pm[lane * sm] : -INFINITY;
-    const float l = lane < n ? pm[lane * sm + 1] : 0.f;
-    const int e = lane < n ? static_cast<int>(pm[lane * sm + 2]) : 0;
-    M = m;
+    // GRP partial loads in flight per group (indices past the last chunk
+    // re-read it and are not added): one memory latency per group; 4 for up
+    // to four chunks, where more would only re-read, else 16
+    auto merge = [&](auto grp) {
+      constexpr int GRP = decltype(grp)::value;
+      u32x2 v[GRP];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float w0 = lane < n ? exp2f(m - M) : 0.f;
-    den = w0 * l;
+      for (int g = 0; g < GRP; ++g) v[g] = raw(min(g, n - 1));
+      const float m = lane < n ? pm[lane * sm] : -INFINITY;
+      const float l = lane < n ? pm[lane * sm + 1] : 0.f;
+      const int e = lane < n ? static_cast<int>(pm[lane * sm + 2]) : 0;
+      M = m;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
-    const float w = ldexpf(w0, e);   // the weight of the stored (scaled) row
-    for (int j = 0; j < n; j += GRP) {
-      if (j > 0) {
-        v0 = load(j);
-        v1 = load(min(j + 1, n - 1));
-        v2 = load(min(j + 2, n - 1));
-        v3 = load(min(j + 3, n - 1));
+      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      const float w0 = lane < n ? exp2f(m - M) : 0.f;
+      den = w0 * l;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+      const float w = ldexpf(w0, e);   // the weight of the stored (scaled) row
+      for (int j = 0; j < n; j += GRP) {
+        if (j > 0) {
+#pragma unroll
+          for (int g = 0; g < GRP; ++g) v[g] = raw(min(j + g, n - 1));
+        }
+#pragma unroll
+        for (int g = 0; g < GRP; ++g)
+          if (j + g < n) acc += __shfl(w, j + g) * cvt(v[g]);
       }
-      acc += __shfl(w, j) * v0;
-      acc += __shfl(w, min(j + 1, 63)) * (j + 1 < n ? v1 : f32x4{0.f, 0.f, 0.f, 0.f});
-      acc += __shfl(w, min(j + 2, 63)) * (j + 2 < n ? v2 : f32x4{0.f, 0.f, 0.f, 0.f});
-      acc += __shfl(w, min(j + 3, 63)) * (j + 3 < n ? v3 : f32x4{0.f, 0.f, 0.f, 0.f});
-    }
+    };
+    if (n <= 4) merge(std::integral_constant<int, 4>{});
+    else merge(std::integral_constant<int, 16>{});
   } else {
     for (int j = 0; j < n; ++j) M = fmaxf(M, pm[j * sm]);
     for (int j = 0; j < n; ++j) {
       const float w = exp2f(pm[j * sm] - M);
       den += w * pm[j * sm + 1];
-      acc += ldexpf(w, static_cast<int>(pm[j * sm + 2])) * load(j);
+      acc += ldexpf(w, static_cast<int>(pm[j * sm + 2])) * cvt(raw(j));
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
