@@ -21,8 +21,17 @@ the shader cycles of every workgroup, its real time and the clock it ran at
 The kernel does the same work on the two paged caches; comparing them
 separates the cycles the kernel needs from the clock the chip runs it at.
 
+With --phases W [W ...] it instead runs each named workload on its own cache
+(contiguous or paged, as the workload defines it) and reports, per phase of
+the kernel, the median shader cycles of the workgroups from the phase stamps
+wave 0 takes: the chunk plan, the prologue (query block, first copies, first
+tile's scores and weights), the steady loop, the general loop (last
+iterations), the last value step with the fallback check, the (m, l) write,
+and the epilogue (output or partials).
+
 Usage: python3 clock_stamps.py [--workload v3_b64_ctx8k] [--calls 200]
-Prints one JSON line per cache and a markdown table.
+       python3 clock_stamps.py --phases v3_b64_ctx8k v3_b8_ctx32k
+Prints one JSON line per cache (or workload) and a markdown table.
 """
 import argparse
 import ctypes
@@ -38,6 +47,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--workload", default="v3_b64_ctx8k")
     ap.add_argument("--calls", type=int, default=200)
+    ap.add_argument("--phases", nargs="+", metavar="WORKLOAD")
     args = ap.parse_args()
 
     import numpy as np
@@ -56,6 +66,9 @@ def main():
     stamps = L.mla_clock_stamps
     stamps.restype, stamps.argtypes = ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]
 
+    if args.phases:
+        phases(L, attn, args.phases, args.calls)
+        return
     cfg = gen.CONFIGS[args.workload]
     assert not cfg.paged and not cfg.topk, "a contiguous dense workload"
     inp = gen.make_inputs(cfg)
@@ -125,6 +138,59 @@ def main():
         print(f"| {r['cache']} | {r['call_us']} | {r['cycles_median']:,} | {r['cycles_per_tile_median']:,} | "
               f"{r['wg_time_us_median']} / {r['wg_time_us_max']} | {r['clock_ghz_median']} "
               f"({r['clock_ghz_min']}..{r['clock_ghz_max']}) |")
+
+
+PHASES = ["plan", "prologue", "steady loop", "general loop", "last value step", "(m, l) write", "epilogue"]
+
+
+def phases(L, attn, workloads, calls):
+    import numpy as np
+    import torch
+    from kv_cache_compression_mla_amd import inputs as gen
+    from kv_cache_compression_mla_amd import mla
+    from kv_cache_compression_mla_amd.step import DeviceStep
+
+    ph = L.mla_phase_stamps
+    ph.restype, ph.argtypes = ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]
+    reset = L.mla_clock_stamps_reset
+    reset.restype, reset.argtypes = ctypes.c_int, []
+    assert calls >= 2
+    rows = []
+    for name in workloads:
+        cfg = gen.CONFIGS[name]
+        assert not cfg.topk, "a dense workload"
+        st = DeviceStep(gen.make_inputs(cfg))
+        st.run()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        for _ in range(calls):
+            rc = attn(ctypes.byref(st.dims), cfg.B, st.q.data_ptr(), ctypes.byref(st.cdesc), st.seq_lens.data_ptr(),
+                      st.max_seq_len, 0, st.o_lat.data_ptr(), st.lse.data_ptr(), st.ws.data_ptr(), st.ws.numel(),
+                      stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(mla.lib().mla_status_str(rc).decode())
+            if _ == calls - 2:
+                # before the last call: only its workgroups with a chunk stamp
+                torch.cuda.synchronize()
+                if reset() != 0:
+                    raise RuntimeError("mla_clock_stamps_reset failed")
+        torch.cuda.synchronize()
+        grid = max(torch.cuda.get_device_properties(0).multi_processor_count, cfg.B)
+        buf = np.zeros((grid, 8), dtype=np.uint64)
+        if ph(buf.ctypes.data, grid) != 0:
+            raise RuntimeError("mla_phase_stamps failed")
+        s = buf[buf[:, 7] > buf[:, 0]].astype(np.float64)
+        total = len(s)
+        d = np.diff(s, axis=1)
+        res = {"workload": name, "workgroups": total, "calls": calls,
+               "cycles_median": int(np.median(s[:, 7] - s[:, 0]))}
+        res.update({k: int(np.median(d[:, i])) for i, k in enumerate(PHASES)})
+        rows.append(res)
+        print(json.dumps(res), flush=True)
+    print("\n| workload | " + " | ".join(PHASES) + " | workgroup |")
+    print("|---|" + "---:|" * (len(PHASES) + 1))
+    for r in rows:
+        print(f"| {r['workload']} | " + " | ".join(f"{r[k]:,}" for k in PHASES) + f" | {r['cycles_median']:,} |")
 
 
 if __name__ == "__main__":

@@ -76,9 +76,17 @@ namespace mla {
 // without it): every attention workgroup records the shader-clock counter
 // (s_memtime, which counts shader cycles) and the 100 MHz real-time counter
 // (s_memrealtime) at its start and at its end, so that clock_stamps.py can
-// report cycles per workgroup and the clock each ran at.
+// report cycles per workgroup and the clock each ran at. Wave 0 also records
+// the shader clock at the boundaries of the kernel's phases (g_phase, eight
+// per workgroup): start, plan done, first tile's scores and weights done,
+// steady loop done, general loop done, last value step and fallback check
+// done, (m, l) written, end.
 constexpr int kStampSlots = 65536;
 __device__ unsigned long long g_clock_stamps[4 * kStampSlots];
+__device__ unsigned long long g_phase[8 * kStampSlots];
+#define MLA_PHASE(i) (phase_t[i] = __builtin_amdgcn_s_memtime())
+#else
+#define MLA_PHASE(i) ((void)0)
 #endif
 namespace {
 
@@ -128,6 +136,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -175,29 +184,50 @@ struct ChunkPlan {
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Cross-lane operations of one fully active wave in VALU instructions only
+// (DPP lane permutations within rows of 16 lanes, the row-pair and
+// half-wave swaps v_permlane16_swap / v_permlane32_swap), not through the
+// LDS permute unit: each step costs a few cycles instead of an LDS round
+// trip, which matters on the dependent chains of the chunk plan.
+// wave_reduce: every lane gets op over all 64 lanes. Each step combines a
+// lane with its partner in an order both partners share, so every lane
+// ends with the same bits (float sums included).
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  auto bits = [](T v) { return __builtin_bit_cast(int, v); };
+  auto val = [](int v) { return __builtin_bit_cast(T, v); };
+  x = op(x, val(__builtin_amdgcn_update_dpp(bits(x), bits(x), 0xB1, 0xf, 0xf, false)));   // lane ^ 1
+  x = op(x, val(__builtin_amdgcn_update_dpp(bits(x), bits(x), 0x4E, 0xf, 0xf, false)));   // lane ^ 2
+  x = op(x, val(__builtin_amdgcn_update_dpp(bits(x), bits(x), 0x141, 0xf, 0xf, false)));  // other quad of 8
+  x = op(x, val(__builtin_amdgcn_update_dpp(bits(x), bits(x), 0x140, 0xf, 0xf, false)));  // other half of 16
+  auto r = __builtin_amdgcn_permlane16_swap(bits(x), bits(x), false, false);   // rows 0|1, 2|3
+  x = op(val(static_cast<int>(r[0])), val(static_cast<int>(r[1])));
+  r = __builtin_amdgcn_permlane32_swap(bits(x), bits(x), false, false);        // halves
+  return op(val(static_cast<int>(r[0])), val(static_cast<int>(r[1])));
 }
+__device__ __forceinline__ int wave_sum(int v) { return wave_reduce(v, [](int a, int b) { return a + b; }); }
+__device__ __forceinline__ int wave_max(int v) { return wave_reduce(v, [](int a, int b) { return max(a, b); }); }
+__device__ __forceinline__ int wave_min(int v) { return wave_reduce(v, [](int a, int b) { return min(a, b); }); }
+// sum of non-negative 64-bit values below 2^55 per lane: 24-bit low parts
+// and the high parts summed separately (64 * 2^24 fits in 31 bits)
 __device__ __forceinline__ long long wave_sum64(long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int lo = __shfl_xor(static_cast<int>(v & 0xffffffffLL), o);
-    const int hi = __shfl_xor(static_cast<int>(v >> 32), o);
-    v += (static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo);
-  }
-  return v;
+  const int lo = wave_sum(static_cast<int>(v & 0xffffff));
+  const int hi = wave_sum(static_cast<int>(v >> 24));
+  return (static_cast<long long>(hi) << 24) + lo;
 }
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+// Inclusive prefix sum over the 64 lanes: within each row of 16 by shifted
+// adds (a lane with no source lane adds 0), then the totals of the rows
+// before it.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // lane - 1 within the row
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // lane - 2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // lane - 4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // lane - 8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
 // Chunks of one sequence of length L, given its target count t >= 1.
@@ -216,24 +246,39 @@ __device__ ChunkPlan plan_chunks(const Params& p, int* scratch, int* res) {
     const int lane = tid;
     for (int i = lane; i < p.B; i += 64) scratch[i] = virt_len(p.seq_lens, i, p.qpt);
     // (LDS writes and reads below are by this wave only, in order)
+    long long sum = 0;
+    int mx = 0, mn = 0x7fffffff;
+    for (int i = lane; i < p.B; i += 64) {
+      const int L = scratch[i];
+      sum += L;
+      mx = max(mx, L);
+      mn = min(mn, L);
+    }
+    const int lmax = wave_max(mx), lmin = wave_min(mn);
     int target_rows = 0;   // balanced: the chunk size C
     if (p.splits == 0) {
-      long long sum = 0;
-      int mx = 0;
-      for (int i = lane; i < p.B; i += 64) {
-        sum += scratch[i];
-        mx = max(mx, scratch[i]);
-      }
       sum = wave_sum64(sum);
-      mx = wave_max(mx);
       const int avg = static_cast<int>((sum + p.grid - 1) / p.grid);
-      int klo = ceil_div(max(MIN_CHUNK, avg), TILE);
-      int khi = max(klo, ceil_div(max(mx, 1), TILE));
-      while (klo < khi) {   // smallest k with sum_b max(1, ceil(L_b / 32k)) <= grid
-        const int mid = (klo + khi) >> 1, c = mid * TILE;
+      // chunks for chunk size 32k: sum_b max(1, ceil(L_b / 32k)), which does
+      // not grow with k
+      auto chunks = [&](int k) {
+        const int c = k * TILE;
         int cnt = 0;
         for (int i = lane; i < p.B; i += 64) cnt += max(1, ceil_div(scratch[i], c));
-        if (wave_sum(cnt) <= p.grid) khi = mid;
+        return wave_sum(cnt);
+      };
+      // the smallest k with chunks(k) <= grid lies in [klo, khi]: no chunk
+      // size below the average fits, and one chunk per sequence always does.
+      // The lower end is tried first: it is the answer for equal lengths.
+      int klo = ceil_div(max(MIN_CHUNK, avg), TILE);
+      int khi = max(klo, ceil_div(max(lmax, 1), TILE));
+      if (klo < khi) {
+        if (chunks(klo) <= p.grid) khi = klo;
+        else ++klo;
+      }
+      while (klo < khi) {
+        const int mid = (klo + khi) >> 1;
+        if (chunks(mid) <= p.grid) khi = mid;
         else klo = mid + 1;
       }
       target_rows = klo * TILE;
@@ -248,13 +293,8 @@ __device__ ChunkPlan plan_chunks(const Params& p, int* scratch, int* res) {
       seq_chunks(L, p.splits > 0 ? p.splits : max(1, ceil_div(L, target_rows)), &rows, &n);
       local += n;
     }
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    const int total = __shfl(incl, 63);
+    const int incl = wave_incl_scan(local, lane);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
     int start = incl - local;
     // Workgroup -> chunk. When every sequence has the same length (so the
     // same chunk count n) and B is a multiple of 8, the n chunks of a
@@ -262,13 +302,6 @@ __device__ ChunkPlan plan_chunks(const Params& p, int* scratch, int* res) {
     // sequences x n chunks), which dispatch places on one XCD, so they read
     // the sequence's query block through that XCD's L2. Otherwise
     // workgroup x takes chunk x. Chunk indices stay in prefix order.
-    int lmin = 0x7fffffff, lmax = 0;
-    for (int i = lane; i < p.B; i += 64) {
-      lmin = min(lmin, scratch[i]);
-      lmax = max(lmax, scratch[i]);
-    }
-    lmin = wave_min(lmin);
-    lmax = wave_max(lmax);
     int g = blockIdx.x;
     if (lmin == lmax && (p.B & 7) == 0) {
       int rows, n;
@@ -503,11 +536,7 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return r;
 }
 
-// Two floats -> packed fp16 pair (lo = a, hi = b), nearest-even.
-__device__ __forceinline__ uint32_t f16x2_bits(float a, float b) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
-}
+// The fp16 value in the low 16 bits of u, as a float (exact).
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t u) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xffffu)));
 }
@@ -542,6 +571,10 @@ void attn_mfma_kernel(Params p) {
   const unsigned long long stamp_t0 = __builtin_amdgcn_s_memtime(), stamp_r0 = __builtin_amdgcn_s_memrealtime();
 #endif
   const ChunkPlan plan = plan_chunks(p, reinterpret_cast<int*>(smem), reinterpret_cast<int*>(smem + LM_OFF));
+#ifdef MLA_CLOCK_STAMPS
+  unsigned long long phase_t[8] = {stamp_t0, 0, 0, 0, 0, 0, 0, 0};
+  MLA_PHASE(1);
+#endif
   if (plan.b < 0) return;             // no chunk for this workgroup
   const int b = plan.b;
   const int bc = p.qpt == 1 ? b : b / p.qpt;   // the cached sequence it reads
@@ -761,6 +794,7 @@ void attn_mfma_kernel(Params p) {
 #pragma unroll
       for (int k = 0; k < SM_STEPS; ++k) soft_step(S, k, tile_nv(0), !fixed_ref, grew, p_off(0));
     }
+    if (!fixed_ref) MLA_PHASE(2);
     // Iteration t: tile t+1 has landed (only the copies of tile t+2 may
     // still fly), every wave has written the weights of tile t and is past
     // tile t-1, whose stages tile t+3 reuses.
@@ -789,6 +823,7 @@ void attn_mfma_kernel(Params p) {
         for (int k = PV_STEPS; k < SM_STEPS; ++k) soft_step(N, k, TILE, false, grew, pb_next);
       }
     }
+    if (!fixed_ref) MLA_PHASE(3);
     for (; t + 1 < ntiles; ++t) {
       if (t + 2 < ntiles) wait_vmcnt<DMA_PER_WAVE>();
       else wait_vmcnt<0>();
@@ -808,6 +843,7 @@ void attn_mfma_kernel(Params p) {
       for (int k = PV_STEPS; k < SM_STEPS; ++k) soft_step(N, k, nv, false, grew, pb_next);
     }
     // last tile: its weights are complete once every wave is here
+    if (!fixed_ref) MLA_PHASE(4);
     block_barrier();
     pv(t, [](int) {});
     return grew;
@@ -846,6 +882,7 @@ void attn_mfma_kernel(Params p) {
   __syncthreads();
   if (__builtin_amdgcn_ballot_w64(grew) != 0 && lane == 0) *wg_flag = 1;
   __syncthreads();
+  MLA_PHASE(5);
   if (*wg_flag != 0) {
     __syncthreads();
     const float m_exact = max_pass();
@@ -872,6 +909,7 @@ void attn_mfma_kernel(Params p) {
     }
   }
   __syncthreads();
+  MLA_PHASE(6);
   // The accumulators are read next; cover the last MFMAs' latency. Each
   // accumulator then passes through an empty asm, so that no copy of it (the
   // compiler's own included) can be placed above the wait.
@@ -896,83 +934,96 @@ void attn_mfma_kernel(Params p) {
   constexpr int OROW16 = 1024 + 16;     // staged fp16 row stride
   static_assert(64 * OROW <= ROPE_OFF, "staged rows must stay below the rotary slots and weight buffers");
   float* hmax = reinterpret_cast<float*>(smem + P_OFF);   // [4 waves][64 rows]
+  // One branch-free path for each kind of output.
+  auto epilogue = [&](auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
 #pragma unroll
-  for (int R = 0; R < (NW + 1) / 2; ++R) {
-    if (!single) {
+    for (int R = 0; R < (NW + 1) / 2; ++R) {
+      // this round's accumulators (head blocks 2R and 2R + 1), read once
+      float x[2][4][16];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int hb = 2 * R + hh;
-        if (hb < NW) {
-          float amax = 0.f;
+      for (int hh = 0; hh < 2; ++hh)
+        if (2 * R + hh < NW)
 #pragma unroll
           for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float x;
-              asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(oacc[NW * c + hb][r]));
-              amax = max2(amax, __builtin_fabsf(x));
+            for (int r = 0; r < 16; ++r)
+              asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[hh][c][r]) : "a"(oacc[NW * c + 2 * R + hh][r]));
+      float sc[2] = {1.f, 1.f};
+      if constexpr (PARTIAL) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          if (2 * R + hh < NW) {
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) amax = max2(amax, __builtin_fabsf(x[hh][c][r]));
+            amax = max_halves(amax);
+            if (h == 0) hmax[64 * w + 32 * hh + l32] = amax;
+          }
+        __syncthreads();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          if (2 * R + hh < NW) {
+            const int row = 32 * hh + l32;
+            const float mx = max2(max2(hmax[row], hmax[64 + row]), max2(hmax[128 + row], hmax[192 + row]));
+            int e;
+            (void)frexpf(mx, &e);   // mx < 2^e (e = 0 for a zero row)
+            sc[hh] = ldexpf(1.f, -e);
+            if (w == 0 && h == 0)
+              p.part_ml[(static_cast<long long>(gi) * p.H + 32 * (2 * R + hh) + l32) * 4 + 2] = static_cast<float>(e);
+          }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          if (2 * R + hh < NW) sc[hh] = 1.f / lm[2 * (32 * (2 * R + hh) + l32) + 1];
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        if (2 * R + hh < NW)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = colbase(4 * w + c) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
+              const float* v = &x[hh][c][4 * g];
+              const float s = sc[hh];
+              if constexpr (PARTIAL) {
+                const f16x2 lo = __builtin_convertvector((f32x2{v[0] * s, v[1] * s}), f16x2);
+                const f16x2 hi = __builtin_convertvector((f32x2{v[2] * s, v[3] * s}), f16x2);
+                *reinterpret_cast<u32x2*>(smem + (32 * hh + l32) * OROW16 + 2 * col) =
+                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+              } else {
+                *reinterpret_cast<f32x4*>(smem + (32 * hh + l32) * OROW + 4 * col) =
+                    f32x4{v[0] * s, v[1] * s, v[2] * s, v[3] * s};
+              }
             }
-          amax = max_halves(amax);
-          if (h == 0) hmax[64 * w + 32 * hh + l32] = amax;
+      __syncthreads();
+      // H = 32 NW, so the row count is a constant of the unrolled round
+      const int nrows = min(64, 32 * NW - 64 * R);
+      if constexpr (PARTIAL) {
+        uint16_t* dst = p.part_o + (static_cast<long long>(gi) * p.H + 64 * R) * DC;
+#pragma unroll
+        for (int k = 0; k < nrows * (DC / 8) / NTHREADS; ++k) {
+          const int idx = tid + NTHREADS * k, row = idx >> 6, piece = idx & 63;
+          __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(smem + row * OROW16 + 16 * piece),
+                                      reinterpret_cast<f32x4*>(dst + row * DC + 8 * piece));
+        }
+      } else {
+        float* dst = p.o_lat + (static_cast<long long>(b) * p.H + 64 * R) * DC;
+#pragma unroll
+        for (int k = 0; k < nrows * (DC / 4) / NTHREADS; ++k) {
+          const int idx = tid + NTHREADS * k, row = idx >> 7, piece = idx & 127;
+          __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(smem + row * OROW + 16 * piece),
+                                      reinterpret_cast<f32x4*>(dst + row * DC + 4 * piece));
         }
       }
       __syncthreads();
     }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int hb = 2 * R + hh;
-      if (hb < NW) {
-        const int head = 32 * hb + l32;
-        float sc;
-        if (single) {
-          sc = 1.f / lm[2 * head + 1];
-        } else {
-          const int row = 32 * hh + l32;
-          const float mx = max2(max2(hmax[row], hmax[64 + row]), max2(hmax[128 + row], hmax[192 + row]));
-          int e;
-          (void)frexpf(mx, &e);   // mx < 2^e (e = 0 for a zero row)
-          sc = ldexpf(1.f, -e);
-          if (w == 0 && h == 0) p.part_ml[(static_cast<long long>(gi) * p.H + head) * 4 + 2] = static_cast<float>(e);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float x[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x[r]) : "a"(oacc[NW * c + hb][r]));
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = colbase(4 * w + c) + 32 * ((2 * g + h) & 3) + 4 * (g >> 1);
-            if (single) {
-              *reinterpret_cast<f32x4*>(smem + (32 * hh + l32) * OROW + 4 * col) =
-                  f32x4{x[4 * g] * sc, x[4 * g + 1] * sc, x[4 * g + 2] * sc, x[4 * g + 3] * sc};
-            } else {
-              *reinterpret_cast<u32x2*>(smem + (32 * hh + l32) * OROW16 + 2 * col) =
-                  u32x2{f16x2_bits(x[4 * g] * sc, x[4 * g + 1] * sc), f16x2_bits(x[4 * g + 2] * sc, x[4 * g + 3] * sc)};
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-    const int nrows = min(64, p.H - 64 * R);
-    if (single) {
-      float* dst = p.o_lat + (static_cast<long long>(b) * p.H + 64 * R) * DC;
-      for (int idx = tid; idx < nrows * (DC / 4); idx += NTHREADS) {
-        const int row = idx >> 7, piece = idx & 127;
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(smem + row * OROW + 16 * piece),
-                                    reinterpret_cast<f32x4*>(dst + row * DC + 4 * piece));
-      }
-    } else {
-      uint16_t* dst = p.part_o + (static_cast<long long>(gi) * p.H + 64 * R) * DC;
-      for (int idx = tid; idx < nrows * (DC / 8); idx += NTHREADS) {
-        const int row = idx >> 6, piece = idx & 63;
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(smem + row * OROW16 + 16 * piece),
-                                    reinterpret_cast<f32x4*>(dst + row * DC + 8 * piece));
-      }
-    }
-    __syncthreads();
-  }
+  };
+  if (single) epilogue(std::false_type{});
+  else epilogue(std::true_type{});
 #ifdef MLA_CLOCK_STAMPS
   if (tid == 0 && blockIdx.x < kStampSlots) {
     unsigned long long* st = g_clock_stamps + 4 * blockIdx.x;
@@ -980,6 +1031,8 @@ void attn_mfma_kernel(Params p) {
     st[1] = __builtin_amdgcn_s_memtime();
     st[2] = stamp_r0;
     st[3] = __builtin_amdgcn_s_memrealtime();
+    phase_t[7] = st[1];
+    for (int i = 0; i < 8; ++i) g_phase[8 * blockIdx.x + i] = phase_t[i];
   }
 #endif
 }
@@ -1022,14 +1075,13 @@ __global__ __launch_bounds__(128) void combine_chunks(Params p) {
       const float m = lane < n ? pm[lane * sm] : -INFINITY;
       const float l = lane < n ? pm[lane * sm + 1] : 0.f;
       const int e = lane < n ? static_cast<int>(pm[lane * sm + 2]) : 0;
-      M = m;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      M = wave_reduce(m, [](float a, float c) { return fmaxf(a, c); });
       const float w0 = lane < n ? exp2f(m - M) : 0.f;
-      den = w0 * l;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+      den = wave_reduce(w0 * l, [](float a, float c) { return a + c; });
       const float w = ldexpf(w0, e);   // the weight of the stored (scaled) row
+      auto weight = [&](int j) {       // chunk j's weight (j uniform), from its lane
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+      };
       for (int j = 0; j < n; j += GRP) {
         if (j > 0) {
 #pragma unroll
@@ -1037,7 +1089,7 @@ __global__ __launch_bounds__(128) void combine_chunks(Params p) {
         }
 #pragma unroll
         for (int g = 0; g < GRP; ++g)
-          if (j + g < n) acc += __shfl(w, j + g) * cvt(v[g]);
+          if (j + g < n) acc += weight(j + g) * cvt(v[g]);
       }
     };
     if (n <= 4) merge(std::integral_constant<int, 4>{});
@@ -1113,5 +1165,23 @@ extern "C" int mla_clock_stamps(unsigned long long* host_dst, int n) {
   if (n < 0 || n > mla::kStampSlots) return static_cast<int>(hipErrorInvalidValue);
   return static_cast<int>(hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(mla::g_clock_stamps),
                                               sizeof(unsigned long long) * 4 * n, 0, hipMemcpyDeviceToHost));
+}
+// Zero every stamp (then only the workgroups of the next launch that have a
+// chunk write theirs).
+extern "C" int mla_clock_stamps_reset(void) {
+  void* a = nullptr;
+  void* b = nullptr;
+  hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(mla::g_clock_stamps));
+  if (e == hipSuccess) e = hipGetSymbolAddress(&b, HIP_SYMBOL(mla::g_phase));
+  if (e == hipSuccess) e = hipMemset(a, 0, sizeof(mla::g_clock_stamps));
+  if (e == hipSuccess) e = hipMemset(b, 0, sizeof(mla::g_phase));
+  return static_cast<int>(e);
+}
+// The phase stamps of workgroups 0..n-1 ([n][8] shader-clock values) of the
+// last attention launch.
+extern "C" int mla_phase_stamps(unsigned long long* host_dst, int n) {
+  if (n < 0 || n > mla::kStampSlots) return static_cast<int>(hipErrorInvalidValue);
+  return static_cast<int>(hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(mla::g_phase),
+                                              sizeof(unsigned long long) * 8 * n, 0, hipMemcpyDeviceToHost));
 }
 #endif

@@ -132,3 +132,51 @@ def test_equal_lengths_put_a_sequences_chunks_on_one_xcd(B, L, splits):
 def test_ragged_lengths_keep_the_identity_mapping():
     lens = [100, 200] * 8
     assert [workgroup_chunk(x, lens, 1) for x in range(16)] == list(range(16))
+
+
+def _plan_cases():
+    rng = np.random.default_rng(5)
+    yield "64x8193", [8193] * 64, 0
+    yield "8x32769", [32769] * 8, 0
+    yield "1x4097", [4097], 0
+    yield "ragged128", [int(x) for x in rng.integers(1024, 16385, 128)], 0
+    yield "ragged128_s3", [int(x) for x in rng.integers(1024, 16385, 128)], 3
+    yield "300_with_zeros", [int(x) if x > 400 else 0 for x in rng.integers(0, 5000, 300)], 0
+    yield "1000_short", [int(x) for x in rng.integers(0, 300, 1000)], 0
+    yield "64_tiny", [int(x) for x in rng.integers(1, 100, 64)], 0
+    yield "70_mixed", [int(x) for x in rng.integers(1, 40000, 70)], 0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,lens,splits", list(_plan_cases()), ids=[c[0] for c in _plan_cases()])
+def test_device_plan_matches_restatement(name, lens, splits):
+    """The plan the attention workgroups compute on the device, read back from
+    the workspace (each sequence's first chunk and chunk count, written by the
+    workgroup holding its first rows) after a call on a poisoned workspace,
+    equals the restatement above. The cache is one shared set of pages (the
+    plan depends on seq_lens alone)."""
+    import torch
+    B, L = len(lens), max(lens)
+    H, d_c, d_R, bs = 128, 512, 64, 64
+    dims = mla.make_dims(7168, H, 128, 128, d_c, d_R, 1536, "bf16")
+    dev = torch.device("cuda")
+    npages = max(1, -(-L // bs))
+    pool = torch.zeros(npages, bs, d_c + d_R, dtype=torch.bfloat16, device=dev)
+    table = torch.arange(npages, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+    q = torch.zeros(B, H, d_c + 2 * d_R, dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty(B, H, d_c, dtype=torch.float32, device=dev)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ws = torch.full((mla.workspace_bytes(dims, B, L, splits),), 0xFF, dtype=torch.uint8, device=dev)
+    mla.mla_decode_attn(dims, q, mla.make_cache(pool, table), seq_lens, L, o_lat, None, ws, splits)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s = min(splits, max(1, -(-L // TILE))) if splits else 0
+    grid = B * s if s else max(cus, B)
+    up = lambda x: (x + 255) // 256 * 256
+    off = up(grid * H * d_c * 2) + up(grid * H * 4 * 4)
+    got = ws[off:off + 8 * B].cpu().numpy().view(np.int32).reshape(B, 2)
+    _, chunks = check(lens, s, grid)
+    for b in range(B):
+        idx = [i for i, c in enumerate(chunks) if c[0] == b]
+        assert (got[b, 0], got[b, 1]) == (idx[0], len(idx)), (name, b, lens[b], got[b], idx[0], len(idx))
+    assert np.isfinite(o_lat.cpu().numpy()).all()
