@@ -598,13 +598,45 @@ void attn_mfma_kernel(Params p) {
   const uint32_t lane_off = 16 * lane;
 
   // Query of this lane's head in MFMA B-operand order: step s, half h holds
-  // columns 16s + 8h .. 16s + 8h + 7.
+  // columns 16s + 8h .. 16s + 8h + 7. A query row is 1280 bytes, five
+  // segments of 256. Loaded coalesced first: load i of a wave brings segment
+  // i / 8 of the four heads 4 (i % 8) .. 4 (i % 8) + 3 of its block, 16 lanes
+  // per head and 16 bytes per lane, lane position p holding piece
+  // (p - head) mod 16 of the segment (eight whole cache lines per load, where
+  // one lane per head would touch 32 lines per load, each four times). The
+  // operand order is then made through LDS (qperm, after the first copies are
+  // issued): steps 8r .. 8r + 7 use exactly loads 8r .. 8r + 7.
   bf16x8 qreg[QK_ALL];
   {
-    const uint16_t* qp = p.q + (static_cast<long long>(b) * p.H + qhead) * QW + 8 * h;
+    const uint16_t* qb = p.q + (static_cast<long long>(b) * p.H + 32 * hq) * QW;
+    const int pos = lane & 15;
 #pragma unroll
-    for (int s = 0; s < QK_ALL; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    for (int i = 0; i < QK_ALL; ++i) {
+      const int hd = 4 * (i % 8) + (lane >> 4);
+      qreg[i] = *reinterpret_cast<const bf16x8*>(qb + hd * QW + 128 * (i / 8) + 8 * ((pos - hd) & 15));
+    }
   }
+  // Operand order through this wave's 8 KiB of LDS in the fourth tile stage
+  // (untouched until tile 3's copy, after the first barrier of the loop), five
+  // rounds: the round's eight loads are written as they came (1 KiB each,
+  // contiguous), then step s = 8r + j of head l32 is read from load 8r + l32 / 4,
+  // head slot l32 % 4, position (2j + h + l32) mod 16, which for the 16 heads
+  // of a read pass are 16 distinct bank groups. Wave-local: LDS operations of
+  // a wave complete in order.
+  static_assert(QK_ALL == 5 * 8 && 2 * QW == 5 * 256, "five rounds of eight loads, five 256-byte segments");
+  static_assert(4 * 8192 <= LAT_STAGE, "the four waves' query staging fits one tile stage");
+  auto qperm = [&]() {
+    char* qs = smem + 3 * LAT_STAGE + 8192 * w;
+#pragma unroll
+    for (int r = 0; r < QK_ALL / 8; ++r) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<bf16x8*>(qs + 1024 * j + 16 * lane) = qreg[8 * r + j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        qreg[8 * r + j] = *reinterpret_cast<const bf16x8*>(qs + 1024 * (l32 >> 2) + 256 * (l32 & 3) +
+                                                           16 * ((2 * j + h + l32) & 15));
+    }
+  };
 
   // O^T accumulators: block NW*c + hb holds columns of value block 4w + c
   // against heads 32hb..32hb+31.
@@ -781,8 +813,15 @@ void attn_mfma_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < NSTAGE - 1; ++j)
       if (j < ntiles) copy_tile(j);
-    // Wait for the query (loaded first) and tile 0; tiles 1 and 2 may still
-    // fly. The loop's waits count only these copies: nothing else in flight.
+    if (!fixed_ref) {
+      // the query loads (issued first) are done; the tile copies may fly
+      if (ntiles >= 3) wait_vmcnt<3 * DMA_PER_WAVE>();
+      else if (ntiles == 2) wait_vmcnt<2 * DMA_PER_WAVE>();
+      else wait_vmcnt<DMA_PER_WAVE>();
+      qperm();
+    }
+    // Wait for tile 0; tiles 1 and 2 may still fly. The loop's waits count
+    // only these copies: nothing else in flight.
     if (ntiles >= 3) wait_vmcnt<2 * DMA_PER_WAVE>();
     else if (ntiles == 2) wait_vmcnt<DMA_PER_WAVE>();
     else wait_vmcnt<0>();
