@@ -40,7 +40,9 @@
 // block of 32 columns covers four runs of 8 columns 32 apart, which makes
 // the transposed reads of 32 lanes tile all 64 banks. All three read
 // patterns are bank-conflict free and every address is one per-lane base
-// plus a compile-time offset.
+// plus a compile-time offset. The query block is loaded coalesced (whole
+// cache lines per load) and put in MFMA operand order through LDS before the
+// first tile lands.
 //
 // Software pipeline (one wave per SIMD): iteration t runs the score MFMAs of
 // tile t+1 with this wave's nine LDS-DMA copies of tile t+3 slotted between
@@ -60,9 +62,10 @@
 // true maximum, and a second full pass uses it as the reference (weights
 // <= 1). The result is the same softmax either way.
 //
-// Context splits: a workgroup covers rows [s*chunk, min((s+1)*chunk, L_b)).
-// With more than one split it writes unnormalised (O, m, l) partials, merged
-// exactly by combine_chunks. O goes out in fp16 with a power-of-two scale
+// Context chunks: every workgroup computes the same chunk plan from seq_lens
+// (plan_chunks) and takes rows [r0, r1) of one sequence. A sequence cut into
+// more than one chunk gets unnormalised (O, m, l) partials, merged exactly
+// by combine_chunks. O goes out in fp16 with a power-of-two scale
 // per (chunk, head): every element of the row is O * 2^-E with 2^E above the
 // row's largest magnitude, so no element overflows and each keeps 11 bits
 // relative to the row's maximum (half the bytes of float32 partials).
