@@ -186,13 +186,14 @@ def test_prefill_argument_errors(L):
 
 def test_prefill_auto_choice(L):
     # The cost model's choice on the swept shape (4 sequences of 4096 rows in a
-    # 4097-row cache): absorbed up to 256 new tokens, materialised from 512.
+    # 4097-row cache): absorbed up to 384 new tokens (366 attended rows per
+    # stored row), materialised from 448 (423).
     d = v3()
     c = mla.MLACache(A, None, 4097, 0, 0, 0)
     MAT, ABS, AUTO = mla.PREFILL_MATERIALIZED, mla.PREFILL_ABSORBED, mla.PREFILL_AUTO
     choose = lambda B, T, msl=4096, cache=c: L.mla_prefill_choose(ctypes.byref(d), B, T, msl, ctypes.byref(cache))
-    assert [choose(4, T) for T in (1, 64, 256)] == [ABS] * 3
-    assert [choose(4, T) for T in (512, 1024, 4096)] == [MAT] * 3
+    assert [choose(4, T) for T in (1, 64, 256, 384)] == [ABS] * 4
+    assert [choose(4, T) for T in (448, 512, 1024, 4096)] == [MAT] * 4
     # B * T above the absorbed kernel's 32768 token entries: materialised
     assert choose(64, 600, 4096, mla.MLACache(A, None, 4097, 0, 0, 0)) == MAT
     # a pool too large to expand in one product (8,960,000 stored rows):
