@@ -8,14 +8,18 @@ synthetic tensors of the DeepSeek-V3 geometry, resident in HBM before timing.
 
 Headline: decode-attention TFLOP/s (algorithmic FLOPs 2*H*(D + d_c) per
 attended row) and latent-cache GB/s (1152 B per attended row) of the
-mla_decode_attn call, both from HIP events recorded on the stream the library
-launches on (created with hipEventReleaseToDevice, the runtime's flag for
-timing the commands between events without a system-scope cache flush); ms_per_step is the whole step (wall clock over the K timed
-steps, whose only events are the two around the attention call) and calls_ms
-the mean time of each of the four calls from a separate untimed pass with
-events between them. The roofline object prices the
-attention call against MI355X's published HBM bandwidth (8 TB/s); the CPU
-baseline times the float64 oracle on a bounded sample of the same workload.
+mla_decode_attn call. The call's kernels stamp HIP events themselves
+(mla_time_next_attn: hipExtLaunchKernel's start and stop events on the stream
+the library launches on), so the timed steps carry no marker commands: attn_ms
+runs from the attention kernel's start to the end of the merge of the chunks
+(combine_chunks), attn_kernel_ms is the attention kernel alone. The roofline
+object prices that kernel, the dominant one, against MI355X's published HBM
+bandwidth (8 TB/s) with its algorithmic bytes (cache rows and q, and o_lat
+when no merge runs); the "call" object prices the whole call (cache, q,
+o_lat, lse). ms_per_step is the whole step (wall clock over the K timed
+steps) and calls_ms the mean time of each of the four calls from a separate
+untimed pass with marker events between them. The CPU baseline times the
+float64 oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--precomposed]
@@ -43,32 +47,35 @@ def log(msg):
 
 def attn_work(cfg, seq_lens):
     """Algorithmic bytes and FLOPs of one attention call (seq_lens: rows
-    attended per sequence; the entry counts for sparse attention)."""
+    attended per sequence; the entry counts for sparse attention): rows,
+    cache bytes, q bytes, o_lat + lse bytes, FLOPs."""
     rows = int(seq_lens.sum())
     row_bytes = cfg.D * 2
     cache_bytes = rows * row_bytes
     q_bytes = cfg.B * cfg.H * (cfg.D + cfg.d_R) * 2     # [q_lat ; q_R ; low term of q_R]
     out_bytes = cfg.B * cfg.H * cfg.d_c * 4 + cfg.B * cfg.H * 4
     flops = rows * 2 * cfg.H * (cfg.D + cfg.d_c)
-    return rows, cache_bytes, cache_bytes + q_bytes + out_bytes, flops
+    return rows, cache_bytes, q_bytes, out_bytes, flops
 
 
 def traffic_from_profile(workload):
-    """HBM bytes per attention call from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source; else None."""
+    """HBM bytes per launch of the attention kernel and per attention call
+    (kernel + merge) from committed rocprofv3 counter runs, if they were taken
+    on the current kernel source; else (None, None)."""
     path = os.path.join(ROOT, "profiles", f"attn_hbm_traffic_{workload}.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     try:
         with open(path) as f:
             prof = json.load(f)
         with open(ATTN_SRC, "rb") as f:
             src_hash = hashlib.sha256(f.read()).hexdigest()
         if prof.get("attn_source_sha256") != src_hash:
-            return None
-        return prof.get("bytes_per_call")
+            return None, None
+        k = prof["kernels"]["attn"]
+        return round(k["fetch_bytes"] + k["write_bytes"]), prof.get("bytes_per_call")
     except Exception:
-        return None
+        return None, None
 
 
 def cpu_baseline(inp, budget_s, topk=None):
@@ -237,6 +244,9 @@ class DeviceEvents:
         ms = self.ct.c_float()
         rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
         if rc != 0:
+            # take the error off the thread, or the next HIP call (torch's
+            # included) reports it as its own
+            self.hip.hipGetLastError()
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
@@ -305,16 +315,22 @@ def main():
     log(f"inputs for {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
     st = DeviceStep(inp, num_splits=args.num_splits, precomposed=args.precomposed)
     attended = st.topk_counts_host if cfg.topk else inp.seq_lens
-    rows, cache_bytes, attn_bytes, attn_flops = attn_work(cfg, attended)
+    rows, cache_bytes, q_bytes, out_bytes, attn_flops = attn_work(cfg, attended)
+    attn_bytes = cache_bytes + q_bytes + out_bytes
     splits = st.splits
+    # a sequence cut into chunks is merged by a second kernel (combine_chunks),
+    # which writes o_lat; otherwise the attention kernel writes it
+    merged = splits > 1
+    kernel_bytes = cache_bytes + q_bytes + (0 if merged else out_bytes)
     log(f"B={cfg.B} rows={rows} splits={splits} kernel={mla.decode_kernel(st.dims)}")
 
     stream = torch.cuda.current_stream()
-    # timed region: K whole steps; the only events in it are the two around
-    # the attention call (each event is a marker packet that costs the
-    # stream a few microseconds, so per-call events would inflate the step)
+    # timed region: K whole steps. The attention call of each step stamps three
+    # events from its own kernel launches (mla_time_next_attn: the attention
+    # kernel's start and end, and the end of the merge), so no marker command
+    # enters the stream and the step runs as it would untimed.
     dev_ev = DeviceEvents(torch)
-    ev = [(dev_ev.create(), dev_ev.create()) for _ in range(args.steps)]
+    ev = [(dev_ev.create(), dev_ev.create(), dev_ev.create()) for _ in range(args.steps)]
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
@@ -323,14 +339,15 @@ def main():
     for k in range(args.steps):
         st.compress_append()
         st.absorb_q()
-        dev_ev.record(ev[k][0], stream)
+        mla.mla_time_next_attn(ev[k][0].value, ev[k][1].value, ev[k][2].value)
         st.decode_attn()
-        dev_ev.record(ev[k][1], stream)
         st.out_proj()
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
-    attn_times = [dev_ev.elapsed_ms(a, b) for a, b in ev]
+    attn_times = [dev_ev.elapsed_ms(a, c) for a, b, c in ev]
+    kernel_times = [dev_ev.elapsed_ms(a, b) for a, b, c in ev]
     attn_ms = float(np.mean(attn_times))
+    kernel_ms = float(np.mean(kernel_times))
     ms_per_step = t_total * 1e3 / args.steps
 
     # per-call breakdown, after the timed region: events between all four calls
@@ -354,8 +371,9 @@ def main():
     copy_gbps = measured_copy_gbps(torch)
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     cache_gbps = cache_bytes / (attn_ms * 1e-3) / 1e9
-    achieved_gbps = attn_bytes / (attn_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(cfg.name)
+    call_gbps = attn_bytes / (attn_ms * 1e-3) / 1e9
+    kernel_gbps = kernel_bytes / (kernel_ms * 1e-3) / 1e9
+    kernel_traffic, call_traffic = traffic_from_profile(cfg.name)
     result = {
         "metric": "MLA decode-attn TFLOP/s + cache GB/s (% roofline), H=128 d_c=512+64, bs64 ctx8K",
         "value": round(tflops, 3),
@@ -375,17 +393,23 @@ def main():
                    "precomposed": bool(args.precomposed)},
         "attn_ms": round(attn_ms, 5),
         "attn_ms_median": round(float(np.median(attn_times)), 5),
+        "attn_kernel_ms": round(kernel_ms, 5),
         "calls_ms": calls_ms,
         "cache_GBps": round(cache_gbps, 1),
-        "pct_hbm_roofline": round(100 * achieved_gbps / HBM_PEAK_GBPS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic,
-                     "kernel": "mla_decode_attn call (attn_mfma_kernel, then combine_chunks, which merges the "
-                               "chunks of every sequence cut into more than one)",
+        "pct_hbm_roofline": round(100 * call_gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": kernel_traffic,
+                     "kernel": "attn_mfma_kernel (algorithmic bytes: cache rows + q"
+                               + (")" if merged else " + o_lat + lse)"),
+                     "bytes": kernel_bytes,
                      "measured_copy_GBps": round(copy_gbps, 1),
-                     "frac_of_copy": round(achieved_gbps / copy_gbps, 4),
-                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+                     "frac_of_copy": round(kernel_gbps / copy_gbps, 4),
+                     "mfma_frac": round(attn_flops / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "call": {"what": "mla_decode_attn, attention kernel start to "
+                         + ("combine_chunks end" if merged else "its end"),
+                 "ms": round(attn_ms, 5), "bytes": attn_bytes, "achieved_GBps": round(call_gbps, 1),
+                 "frac": round(call_gbps / HBM_PEAK_GBPS, 4), "traffic": call_traffic},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

@@ -403,6 +403,25 @@ size_t mla_cache_row_bytes(const mla_dims* dims);
  * 2 = general kernel (any other geometry, fp32 or bf16), 0 = bad dims. */
 int32_t mla_decode_kernel(const mla_dims* dims);
 
+/*
+ * mla_time_next_attn -- kernel timing of the next attention call. The next
+ * mla_decode_attn, mla_decode_attn_sparse or mla_decode_attn_noalloc call
+ * made on the calling host thread stamps kernel_start with the start of its
+ * attention kernel, kernel_end with that kernel's end and call_end with the
+ * end of the call's last kernel (the merge of a sequence's chunks, when it
+ * runs). The bf16 MFMA path launches its kernels with hipExtLaunchKernel's
+ * start and stop events, so no marker command enters the stream; the general
+ * kernel (mla_decode_kernel = 2) records the events as markers around its
+ * launches instead.
+ *   kernel_start, kernel_end, call_end  hipEvent_t handles created by the
+ *            caller with timing enabled, or NULL to leave one out; the
+ *            caller owns them and reads them with hipEventElapsedTime
+ * The setting holds for one attention call and is cleared by it, whether
+ * that call succeeds or not; mla_prefill_attn does not take it. A call that
+ * enqueues nothing (an error status) stamps nothing. Returns MLA_OK.
+ */
+mla_status mla_time_next_attn(void* kernel_start, void* kernel_end, void* call_end);
+
 /* Text for a status code (static storage). */
 const char* mla_status_str(int32_t status);
 

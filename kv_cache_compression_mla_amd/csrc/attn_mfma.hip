@@ -71,6 +71,8 @@
 // relative to the row's maximum (half the bytes of float32 partials).
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "mla_internal.hpp"
 
 namespace mla {
@@ -1152,6 +1154,18 @@ __global__ __launch_bounds__(128) void combine_chunks(Params p) {
     p.lse[b * p.H + head] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
+// A launch whose start and end stamp the given events when either is set
+// (hipExtLaunchKernel's kernel-timing events, which put no marker command in
+// the stream), a plain launch otherwise.
+template <typename Kernel>
+void launch_timed(Kernel kernel, dim3 grid, int threads, hipStream_t stream, hipEvent_t start, hipEvent_t end,
+                  const Params& p) {
+  if (start || end)
+    hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, start, end, 0, p);
+  else
+    kernel<<<grid, threads, 0, stream>>>(p);
+}
+
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
@@ -1179,12 +1193,18 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.grid);
   const int pm = a.indices ? (a.block_table ? GATHER_PAGED : GATHER_CONTIG)
                            : (!a.block_table ? CONTIG : (a.block_size >= 8 ? PAGED8 : PAGED_SMALL));
-#define MLA_ATTN_LAUNCH(NW)                                                                       \
-  if (pm == CONTIG) attn_mfma_kernel<NW, CONTIG><<<grid, NTHREADS, 0, stream>>>(p);               \
-  else if (pm == PAGED8) attn_mfma_kernel<NW, PAGED8><<<grid, NTHREADS, 0, stream>>>(p);          \
-  else if (pm == PAGED_SMALL) attn_mfma_kernel<NW, PAGED_SMALL><<<grid, NTHREADS, 0, stream>>>(p); \
-  else if (pm == GATHER_CONTIG) attn_mfma_kernel<NW, GATHER_CONTIG><<<grid, NTHREADS, 0, stream>>>(p); \
-  else attn_mfma_kernel<NW, GATHER_PAGED><<<grid, NTHREADS, 0, stream>>>(p);
+  // with one workgroup per sequence every sequence has a single chunk and no
+  // merge runs; the kernel is then the call's last
+  const bool merge = a.grid > a.B;
+  hipEvent_t k_end = a.t_kernel_end ? a.t_kernel_end : (merge ? nullptr : a.t_call_end);
+#define MLA_ATTN_LAUNCH(NW)                                                                                     \
+  if (pm == CONTIG) launch_timed(attn_mfma_kernel<NW, CONTIG>, grid, NTHREADS, stream, a.t_start, k_end, p);     \
+  else if (pm == PAGED8) launch_timed(attn_mfma_kernel<NW, PAGED8>, grid, NTHREADS, stream, a.t_start, k_end, p); \
+  else if (pm == PAGED_SMALL)                                                                                   \
+    launch_timed(attn_mfma_kernel<NW, PAGED_SMALL>, grid, NTHREADS, stream, a.t_start, k_end, p);               \
+  else if (pm == GATHER_CONTIG)                                                                                 \
+    launch_timed(attn_mfma_kernel<NW, GATHER_CONTIG>, grid, NTHREADS, stream, a.t_start, k_end, p);             \
+  else launch_timed(attn_mfma_kernel<NW, GATHER_PAGED>, grid, NTHREADS, stream, a.t_start, k_end, p);
   switch (a.H / 32) {
     case 1: MLA_ATTN_LAUNCH(1) break;
     case 2: MLA_ATTN_LAUNCH(2) break;
@@ -1193,8 +1213,11 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
 #undef MLA_ATTN_LAUNCH
-  // with one workgroup per sequence every sequence has a single chunk
-  if (a.grid > a.B) combine_chunks<<<dim3(a.B * a.H), 128, 0, stream>>>(p);
+  if (merge) launch_timed(combine_chunks, dim3(a.B * a.H), 128, stream, nullptr, a.t_call_end, p);
+  else if (a.t_kernel_end && a.t_call_end) {
+    const hipError_t e = hipEventRecord(a.t_call_end, stream);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 

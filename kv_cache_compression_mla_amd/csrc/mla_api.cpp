@@ -17,6 +17,18 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Events for the next attention call on this thread (mla_time_next_attn).
+struct AttnTiming {
+  hipEvent_t start = nullptr, kernel_end = nullptr, call_end = nullptr;
+};
+thread_local AttnTiming g_attn_timing;
+
+AttnTiming take_attn_timing() {
+  const AttnTiming t = g_attn_timing;
+  g_attn_timing = AttnTiming{};
+  return t;
+}
+
 mla_status fail(mla_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -425,7 +437,7 @@ namespace {
 mla_status decode_attn_impl(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
                             const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_lat,
                             float* lse, void* ws, size_t ws_bytes, void* stream, const int32_t* indices,
-                            int32_t topk, int32_t qpt = 1) {
+                            int32_t topk, int32_t qpt = 1, AttnTiming tm = AttnTiming{}) {
   MLA_TRY(check_dims(dims));
   if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
   if (max_seq_len < 0 || num_splits < 0) return fail(MLA_ERR_SHAPE, "negative max_seq_len or num_splits");
@@ -469,6 +481,9 @@ mla_status decode_attn_impl(const mla_dims* dims, int32_t B, const void* q, cons
   a.indices = indices;
   a.topk = topk;
   a.qpt = qpt;
+  a.t_start = tm.start;
+  a.t_kernel_end = tm.kernel_end;
+  a.t_call_end = tm.call_end;
   if (mfma) {
     // the device plans the chunks (balanced when num_splits is 0) and merges them
     const int s = mfma_splits(num_splits, max_seq_len);
@@ -494,8 +509,12 @@ mla_status decode_attn_impl(const mla_dims* dims, int32_t B, const void* q, cons
     a.splits = 1;
     a.chunk = 1;
   }
+  // the general kernel takes the timing events as markers around its launches
+  if (tm.start) MLA_TRY(hip_status(hipEventRecord(tm.start, st), "timing event"));
   MLA_TRY(hip_status(mla::launch_attn_generic(a, st), "attention launch"));
+  if (tm.kernel_end) MLA_TRY(hip_status(hipEventRecord(tm.kernel_end, st), "timing event"));
   if (a.splits > 1) MLA_TRY(hip_status(mla::launch_attn_combine(a, st), "combine launch"));
+  if (tm.call_end) MLA_TRY(hip_status(hipEventRecord(tm.call_end, st), "timing event"));
   return ok();
 }
 
@@ -760,19 +779,28 @@ mla_status mla_prefill_attn(const mla_dims* dims, int32_t B, int32_t T, const vo
 mla_status mla_decode_attn(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
                            const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_lat,
                            float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const AttnTiming tm = take_attn_timing();
   return decode_attn_impl(dims, B, q, cache, seq_lens, max_seq_len, num_splits, o_lat, lse, ws, ws_bytes, stream,
-                          nullptr, 0);
+                          nullptr, 0, 1, tm);
+}
+
+mla_status mla_time_next_attn(void* kernel_start, void* kernel_end, void* call_end) {
+  g_attn_timing.start = static_cast<hipEvent_t>(kernel_start);
+  g_attn_timing.kernel_end = static_cast<hipEvent_t>(kernel_end);
+  g_attn_timing.call_end = static_cast<hipEvent_t>(call_end);
+  return ok();
 }
 
 mla_status mla_decode_attn_sparse(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
                                   const int32_t* indices, int32_t topk, const int32_t* counts, int32_t num_splits,
                                   float* o_lat, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const AttnTiming tm = take_attn_timing();
   if (topk <= 0) return fail(MLA_ERR_SHAPE, "decode_attn_sparse: topk must be positive");
   if (!indices || !counts) return fail(MLA_ERR_NULL, "decode_attn_sparse: NULL indices or counts");
   if ((reinterpret_cast<uintptr_t>(indices) | reinterpret_cast<uintptr_t>(counts)) & 3)
     return fail(MLA_ERR_ALIGN, "decode_attn_sparse: indices and counts must be 4-byte aligned");
   return decode_attn_impl(dims, B, q, cache, counts, topk, num_splits, o_lat, lse, ws, ws_bytes, stream, indices,
-                          topk);
+                          topk, 1, tm);
 }
 
 mla_status mla_check_indices(const mla_dims* dims, int32_t B, const mla_cache* cache, const int32_t* pos,
@@ -1024,6 +1052,7 @@ mla_status scratch_address(void** out) {
 extern "C" mla_status mla_decode_attn_noalloc(const mla_dims* dims, int32_t B, const void* q, const mla_cache* cache,
                                               const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits,
                                               float* o_lat, float* lse, void* stream) {
+  const AttnTiming tm = take_attn_timing();
   MLA_TRY(check_dims(dims));
   if (B <= 0) return fail(MLA_ERR_SHAPE, "B must be positive");
   if (max_seq_len < 0 || num_splits < 0) return fail(MLA_ERR_SHAPE, "negative max_seq_len or num_splits");
@@ -1034,5 +1063,5 @@ extern "C" mla_status mla_decode_attn_noalloc(const mla_dims* dims, int32_t B, c
   void* ws = nullptr;
   MLA_TRY(scratch_address(&ws));
   return decode_attn_impl(dims, B, q, cache, seq_lens, max_seq_len, num_splits, o_lat, lse, ws,
-                          MLA_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
+                          MLA_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0, 1, tm);
 }

@@ -180,6 +180,10 @@ struct AttnArgs {
   // per cached sequence; entry b attends the first virt_len(...) rows of
   // sequence b / qpt
   int qpt = 1;
+  // kernel-timing events for one call (mla_time_next_attn), NULL for none:
+  // t_start takes the attention kernel's start, t_kernel_end its end and
+  // t_call_end the end of the call's last kernel
+  hipEvent_t t_start = nullptr, t_kernel_end = nullptr, t_call_end = nullptr;
 };
 
 // Rows attended by entry b: seq_lens[b] for decode (qpt = 1); with qpt query

@@ -79,6 +79,7 @@ _SIGS = {
     "mla_check_indices": (ctypes.c_int, [ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.POINTER(MLACache)]
                           + [ctypes.c_void_p] * 2 + [ctypes.c_int32] + [ctypes.c_void_p] * 2 + [ctypes.c_int32]
                           + [ctypes.c_void_p]),
+    "mla_time_next_attn": (ctypes.c_int, [ctypes.c_void_p] * 3),
     "mla_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -238,6 +239,13 @@ def mla_decode_attn_sparse(dims, q, cache: MLACache, indices, counts, o_lat, lse
         ctypes.byref(dims), B, _ptr(q, dt, "q"), ctypes.byref(cache), _ptr(indices, torch.int32, "indices"),
         topk, _ptr(counts, torch.int32, "counts"), int(num_splits), _ptr(o_lat, torch.float32, "o_lat"),
         _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"), wsz, _stream(stream)), "mla_decode_attn_sparse")
+
+
+def mla_time_next_attn(kernel_start=None, kernel_end=None, call_end=None):
+    """Stamp hipEvent_t handles (ints, or None to leave one out) with the next
+    attention call's kernel start, kernel end and call end on this thread."""
+    conv = lambda e: None if e is None else ctypes.c_void_p(int(e))
+    _check(lib().mla_time_next_attn(conv(kernel_start), conv(kernel_end), conv(call_end)), "mla_time_next_attn")
 
 
 def mla_out_proj(dims, o_lat, W_UV, W_O, o_heads, out, ws, stream=None):
