@@ -161,7 +161,7 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t B, const void* h_t,
  *              workgroup; the chunks of a sequence are merged exactly
  *              afterwards. Automatic (bf16 MFMA path, the V3 geometry): the
  *              device reads seq_lens and picks the smallest chunk size (at
- *              least 256 rows) whose chunk count fits one workgroup per
+ *              least 128 rows) whose chunk count fits one workgroup per
  *              compute unit (or per sequence, if B is larger), so a ragged
  *              batch is balanced. Other geometries cut every sequence into
  *              the same number of equal chunks of max_seq_len.
