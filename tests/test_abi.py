@@ -107,6 +107,11 @@ def test_decode_attn_argument_errors(L):
     assert call(cache=mla.MLACache(A, None, 0, 0, 0, 0)) == SHAPE
     assert call(cache=mla.MLACache(A, A, 0, 48, 4, 10)) == UNSUPPORTED   # block size not 2^k
     assert call(cache=mla.MLACache(A, A, 0, 64, 1, 10), maxlen=65) == SHAPE
+    # the MFMA path's limits: 32768 sequences (its chunk plan keeps one int per
+    # sequence in LDS) and 2^22 workgroups
+    assert call(B=32769, splits=1, wsb=1 << 40) == UNSUPPORTED
+    big = mla.MLACache(A, None, 1 << 20, 0, 0, 0)
+    assert call(B=32768, splits=200, maxlen=1 << 20, cache=big, wsb=1 << 50) == UNSUPPORTED
     assert "capacity" in L.mla_last_error().decode() or True
 
 

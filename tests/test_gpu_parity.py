@@ -329,6 +329,50 @@ def check_attention(inp, st, q_bits, label, seqs=None):
         assert e_o <= tol(cfg) and e_l <= tol(cfg), (label, b, e_o, e_l)
 
 
+def test_largest_batch_of_the_mfma_kernel():
+    """B = 32768 sequences, the largest batch the MFMA attention takes (its
+    chunk plan keeps one int per sequence in LDS and each lane of the planning
+    wave walks 512 sequences), with 32 heads and ragged contexts of 0 to 16
+    rows: one workgroup per sequence. Workspace filled with 0xFF bytes and
+    outputs with NaN first. Every output finite, empty sequences give zeros
+    and lse = -inf, and 48 sampled sequences (the first and the last among
+    them) match the oracle."""
+    B, H, cap, D, d_c = 32768, 32, 16, 576, 512
+    rng = np.random.default_rng(2024)
+    lens = rng.integers(0, cap + 1, size=B)
+    lens[::97] = 0
+    lens[0], lens[-1] = cap, 1
+    say("max batch: drawing inputs")
+    cache_bits = gen._draw(rng, (B, cap, D), 1.7, "bf16")
+    q_bits = gen._draw(rng, (B, H, D), 0.5, "bf16")
+    dims = mla.make_dims(7168, H, 128, 128, d_c, 64, 1536, "bf16")
+    q = query_rows(q_bits, V3)
+    cache = to_device(cache_bits, "bf16")
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o_lat = torch.full((B, H, d_c), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((mla.workspace_bytes(dims, B, cap, 0),), 0xFF, dtype=torch.uint8, device="cuda")
+    say(f"max batch: B={B} H={H} rows={int(lens.sum())} workspace {ws.numel()} bytes")
+    mla.mla_decode_attn(dims, q, mla.make_cache(cache), seq_lens, cap, o_lat, lse, ws, 0)
+    torch.cuda.synchronize()
+    o, l = o_lat.cpu().numpy(), lse.cpu().numpy()
+    empty = lens == 0
+    assert np.isfinite(o).all()
+    assert (o[empty] == 0).all() and np.isneginf(l[empty]).all()
+    assert np.isfinite(l[~empty]).all()
+    scale = 1.0 / np.sqrt(128 + 64)
+    sample = sorted({0, B - 1} | set(int(x) for x in rng.choice(np.flatnonzero(~empty), 46, replace=False)))
+    for b in sample:
+        n = int(lens[b])
+        q64 = gen.to_f64(q_bits[b], "bf16")
+        rows = gen.to_f64(cache_bits[b, :n], "bf16")
+        ref_o, ref_l = om.attend_absorbed(q64[:, :d_c], q64[:, d_c:], rows, scale)
+        e_o = rel_err(o[b], ref_o)
+        e_l = np.abs(l[b] - ref_l).max() / max(np.abs(ref_l).max(), 1.0)
+        assert e_o <= 1e-2 and e_l <= 1e-2, (b, n, e_o, e_l)
+    say(f"max batch: {len(sample)} sampled sequences within 1e-2 of the oracle")
+
+
 def test_growing_scores_take_the_exact_fallback():
     """Scores that grow by far more than 2^32 over the context (later rows
     scaled up) send the kernel to its exact two-pass path; the result still
